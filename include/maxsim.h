@@ -1,0 +1,130 @@
+/*
+ * maxsim.h -- C ABI of the MI355X (gfx950) MaxSim rerank library, libmaxsim.so.
+ *
+ * Operation (Flash-MaxSim rerank page, docs.vllm.ai,
+ * vllm.v1.pool.flash_maxsim.flash_maxsim_rerank: the module description and the
+ * parameters and return value of `flash_maxsim_rerank_direct`): one query Q of Lq
+ * token rows, each d wide, is scored against B documents whose token rows sit in a
+ * packed row tensor. Document i is the run of doc_lengths[i] consecutive rows that
+ * starts at row doc_offsets[i]; documents may be scattered, in any order, with
+ * unrelated rows between them, and may overlap. For each document
+ *
+ *     scores[i] = sum over q < Lq of  max over t < doc_lengths[i] of  Q[q] . row(doc_offsets[i] + t)
+ *
+ * computed from fp16 or bf16 inputs with fp32 products and sums. Nothing is padded
+ * or copied and no [B, Lq, len] similarity tensor is formed.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers named Q, docs, doc_offsets, doc_lengths, scores and workspace are
+ *     DEVICE pointers (any allocator, including PyTorch's caching allocator). The
+ *     caller owns every buffer; the library keeps no pointer after the call returns.
+ *   - Q: [Lq, d] row-major, contiguous, same element format as docs, 16-byte aligned.
+ *   - docs: rows of `stride` elements (row r starts at element r*stride), unit column
+ *     stride, 16-byte aligned. Only columns 0..d-1 of rows inside documents are read;
+ *     every other row or column may hold anything, NaN included.
+ *   - doc_offsets, doc_lengths: int32 [B]. Row addresses are formed in 64 bits, so
+ *     offset*stride may exceed 2^31 (the page widens the offset before multiplying;
+ *     kernel section `_maxsim_rerank_kernel`).
+ *   - scores: fp32 [B]; every element is written exactly once. It must not alias the
+ *     inputs.
+ *   - stream: a hipStream_t passed as void* (NULL = the default stream). Work is
+ *     enqueued on it and the call returns without waiting; the caller synchronises.
+ *     No entry point reads device memory on the host.
+ *   - Special values: B == 0 writes nothing; Lq == 0 gives scores 0 (an empty sum);
+ *     a document of length 0 gives -inf (its max is over no rows, as in the page's
+ *     kernel, whose running max starts at minus infinity).
+ *   - Preconditions that are not checked (checking would read device memory):
+ *     0 <= doc_offsets[i], 0 <= doc_lengths[i], and doc_offsets[i] + doc_lengths[i]
+ *     rows lie inside the docs allocation. Breaking them is undefined behaviour.
+ *   - Return value: MAXSIM_OK, or an error code; on any error nothing has been
+ *     enqueued, except MAXSIM_ERR_HIP, which reports a failed HIP call (allocation or
+ *     launch) after which the contents of scores are unspecified.
+ *
+ * Supported envelope (MAXSIM_ERR_UNSUPPORTED outside it): 1 <= d <= 256 with
+ * d % 8 == 0; Lq <= 256; stride % 8 == 0 and stride <= 2^24; Q and docs 16-byte
+ * aligned (each lane reads 8 consecutive elements, 16 bytes, of one row at a time).
+ */
+#ifndef MAXSIM_H
+#define MAXSIM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Symbols of this header are the library's only exports. */
+#if defined(__GNUC__) || defined(__clang__)
+#define MAXSIM_API __attribute__((visibility("default")))
+#else
+#define MAXSIM_API
+#endif
+
+/* Status codes. */
+#define MAXSIM_OK 0
+#define MAXSIM_ERR_INVALID_ARG 1 /* null pointer, negative size, stride < d, bad dtype  */
+#define MAXSIM_ERR_UNSUPPORTED 2 /* outside the supported envelope above                */
+#define MAXSIM_ERR_HIP 3         /* a HIP call failed (no device, allocation, launch)   */
+#define MAXSIM_ERR_WORKSPACE 4   /* caller workspace null, misaligned or too small      */
+
+/* Element formats of Q and docs for the staged entry points. */
+#define MAXSIM_F16 0
+#define MAXSIM_BF16 1
+
+/*
+ * MaxSim scores, fp16 Q and docs (IEEE binary16).
+ * Allocates its scratch space stream-ordered (hipMallocAsync / hipFreeAsync on
+ * `stream`), so concurrent calls on different streams do not interfere.
+ */
+MAXSIM_API int maxsim_rerank(const void *Q, int32_t Lq, int32_t d,
+                  const void *docs, int64_t stride,
+                  const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                  float *scores, void *stream);
+
+/* Same as maxsim_rerank, bf16 Q and docs (computed in bf16, never converted). */
+MAXSIM_API int maxsim_rerank_bf16(const void *Q, int32_t Lq, int32_t d,
+                       const void *docs, int64_t stride,
+                       const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                       float *scores, void *stream);
+
+/* Static, NUL-terminated description of a status code (never NULL). */
+MAXSIM_API const char *maxsim_status_string(int status);
+
+/*
+ * Staged form of the same operation, with a caller-owned workspace, for callers that
+ * manage scratch memory themselves or time the two stages apart.
+ *
+ * maxsim_workspace_size: bytes of device workspace that maxsim_plan/maxsim_score need
+ *   for these sizes on the current device (depends on the device's compute-unit
+ *   count). Writes *bytes. Queries the current device: MAXSIM_ERR_HIP without one.
+ *
+ * maxsim_plan: the length-binned doc schedule. Reads doc_offsets and doc_lengths
+ *   and writes the schedule into `workspace` (two kernel launches on `stream`).
+ *   The workspace must be 256-byte aligned and at least maxsim_workspace_size bytes.
+ *
+ * maxsim_score: the scores. Reads the schedule that maxsim_plan wrote into the same
+ *   workspace earlier on the same stream, with the same Lq, d and B, and writes
+ *   scores (one kernel launch). dtype is MAXSIM_F16 or MAXSIM_BF16.
+ *
+ * A workspace must not be shared by work that may run concurrently.
+ */
+MAXSIM_API int maxsim_workspace_size(int32_t Lq, int32_t d, int32_t B, size_t *bytes);
+
+MAXSIM_API int maxsim_plan(const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                int32_t Lq, int32_t d,
+                void *workspace, size_t workspace_bytes, void *stream);
+
+MAXSIM_API int maxsim_score(int dtype, const void *Q, int32_t Lq, int32_t d,
+                 const void *docs, int64_t stride,
+                 const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                 float *scores, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Library version as major*10000 + minor*100 + patch. */
+MAXSIM_API int maxsim_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MAXSIM_H */

@@ -1,0 +1,27 @@
+"""MI355X (gfx950) MaxSim late-interaction rerank.
+
+One query Q[Lq, d] is scored against B variable-length documents read in place from a
+packed, possibly scattered row tensor by per-document (offset, length) pairs:
+score_i = sum over query rows of the best dot product with any of document i's rows
+(Flash-MaxSim rerank page, docs.vllm.ai, vllm.v1.pool.flash_maxsim.flash_maxsim_rerank).
+
+The computation lives in libmaxsim.so (hand-written HIP, C ABI in include/maxsim.h);
+this package is its ctypes binding. Build the library with
+``python -m late_interaction_reranking_amd.build``.
+"""
+
+from .maxsim import (  # noqa: F401
+    MAXSIM_BF16,
+    MAXSIM_F16,
+    MaxSimError,
+    library_path,
+    load,
+    maxsim_plan,
+    maxsim_rerank,
+    maxsim_rerank_bf16,
+    maxsim_score,
+    maxsim_status_string,
+    maxsim_version,
+    maxsim_workspace_size,
+    rerank,
+)

@@ -1,0 +1,454 @@
+// C ABI of the MaxSim rerank library (declared in include/maxsim.h): argument checks,
+// the plan (length-binned doc schedule) kernels, and the launch of the score kernel.
+#include "maxsim.h"
+
+#include <mutex>
+
+#include "maxsim_common.h"
+
+using namespace maxsim;
+
+// Instance lookups, one per (format, K-steps) file built from maxsim_score_inst.hip.
+#define MAXSIM_DECLARE_LOOKUPS(fmt)                                                 \
+    const void *maxsim_score_kernel_##fmt##_k1(int);                               \
+    const void *maxsim_score_kernel_##fmt##_k2(int);                               \
+    const void *maxsim_score_kernel_##fmt##_k3(int);                               \
+    const void *maxsim_score_kernel_##fmt##_k4(int);                               \
+    const void *maxsim_score_kernel_##fmt##_k5(int);                               \
+    const void *maxsim_score_kernel_##fmt##_k6(int);                               \
+    const void *maxsim_score_kernel_##fmt##_k7(int);                               \
+    const void *maxsim_score_kernel_##fmt##_k8(int);                               \
+    const void *maxsim_score_kernel_##fmt(int nks, int nqt)                        \
+    {                                                                              \
+        switch (nks) {                                                             \
+        case 1: return maxsim_score_kernel_##fmt##_k1(nqt);                        \
+        case 2: return maxsim_score_kernel_##fmt##_k2(nqt);                        \
+        case 3: return maxsim_score_kernel_##fmt##_k3(nqt);                        \
+        case 4: return maxsim_score_kernel_##fmt##_k4(nqt);                        \
+        case 5: return maxsim_score_kernel_##fmt##_k5(nqt);                        \
+        case 6: return maxsim_score_kernel_##fmt##_k6(nqt);                        \
+        case 7: return maxsim_score_kernel_##fmt##_k7(nqt);                        \
+        case 8: return maxsim_score_kernel_##fmt##_k8(nqt);                        \
+        default: return nullptr;                                                   \
+        }                                                                          \
+    }
+MAXSIM_DECLARE_LOOKUPS(f16)
+MAXSIM_DECLARE_LOOKUPS(bf16)
+#undef MAXSIM_DECLARE_LOOKUPS
+
+namespace {
+
+// ---------------------------------------------------------------- plan kernels
+//
+// The schedule: docs grouped by tile-count bin (bin_of), highest bin first, docs of one
+// bin in index order. The score kernel hands them out in that order, so the longest
+// docs start first and the short ones fill in the tail.
+//
+// Pass 1 (count) writes, per plan block, the number of its docs in each bin and the
+// sum of their tile counts; it also zeroes the score kernel's counters. Pass 2
+// (scatter) sums those rows to get each bin's start and the block's place inside it,
+// then writes every doc's descriptor at its slot. Block 0 of pass 2 also writes the
+// bin totals and the total tile count to the header.
+
+__device__ __forceinline__ uint32_t tiles_of(int32_t len)
+{
+    return len > 0 ? ((uint32_t)len + (kTileRows - 1)) / kTileRows : 0u;
+}
+
+__global__ void __launch_bounds__(kPlanBlock)
+plan_count_kernel(const int32_t *__restrict__ lengths, int32_t B, uint32_t docs_per_block,
+                  uint32_t *__restrict__ hist, uint32_t *__restrict__ arrive, uint32_t n_arrive,
+                  Header *__restrict__ hdr)
+{
+    __shared__ uint32_t cnt[kNumBins];
+    __shared__ unsigned long long tiles;
+    if (threadIdx.x < kNumBins) cnt[threadIdx.x] = 0;
+    if (threadIdx.x == 0) tiles = 0;
+    __syncthreads();
+
+    const int64_t first = (int64_t)blockIdx.x * docs_per_block;
+    const int64_t last = first + docs_per_block < (int64_t)B ? first + docs_per_block : (int64_t)B;
+    unsigned long long my_tiles = 0;
+    for (int64_t i = first + threadIdx.x; i < last; i += kPlanBlock) {
+        const uint32_t nt = tiles_of(lengths[i]);
+        atomicAdd(&cnt[bin_of(nt)], 1u);
+        my_tiles += nt;
+    }
+    for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
+    if ((threadIdx.x & (kWave - 1)) == 0) atomicAdd(&tiles, my_tiles);
+    __syncthreads();
+
+    uint32_t *row = hist + (size_t)blockIdx.x * kHistStride;
+    if (threadIdx.x < kNumBins) row[threadIdx.x] = cnt[threadIdx.x];
+    if (threadIdx.x == kNumBins) row[kNumBins] = (uint32_t)tiles;
+    if (threadIdx.x == kNumBins + 1) row[kNumBins + 1] = (uint32_t)(tiles >> 32);
+
+    for (uint32_t e = blockIdx.x * kPlanBlock + threadIdx.x; e < n_arrive; e += gridDim.x * kPlanBlock)
+        arrive[e] = 0;
+    if (blockIdx.x == 0 && threadIdx.x == 0) hdr->claim = 0;
+}
+
+__global__ void __launch_bounds__(kPlanBlock)
+plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restrict__ lengths,
+                    int32_t B, uint32_t docs_per_block, const uint32_t *__restrict__ hist,
+                    uint32_t nblocks, Header *__restrict__ hdr, DocDesc *__restrict__ desc)
+{
+    constexpr int kRowGroups = kPlanBlock / kHistStride;  // 32
+    __shared__ unsigned long long part_tot[kRowGroups][kHistStride];
+    __shared__ uint32_t part_before[kRowGroups][kHistStride];
+    __shared__ uint32_t bin_next[kNumBins];  // next free slot of each bin for this block
+    __shared__ uint32_t wave_cnt[kPlanBlock / kWave][kNumBins];
+
+    // Column c of the hist table summed over all blocks, and over blocks before ours.
+    {
+        const int c = threadIdx.x % kHistStride;
+        const int rg = threadIdx.x / kHistStride;
+        unsigned long long tot = 0;
+        uint32_t before = 0;
+        for (uint32_t k = rg; k < nblocks; k += kRowGroups) {
+            const uint32_t v = hist[(size_t)k * kHistStride + c];
+            tot += v;
+            if (k < blockIdx.x) before += v;
+        }
+        part_tot[rg][c] = tot;
+        part_before[rg][c] = before;
+    }
+    __syncthreads();
+    if (threadIdx.x < kHistStride) {
+        const int c = threadIdx.x;
+        unsigned long long tot = 0;
+        uint32_t before = 0;
+        for (int rg = 0; rg < kRowGroups; ++rg) {
+            tot += part_tot[rg][c];
+            before += part_before[rg][c];
+        }
+        part_tot[0][c] = tot;
+        part_before[0][c] = before;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t start = 0;  // bins in descending order
+        for (int b = kNumBins - 1; b >= 0; --b) {
+            bin_next[b] = start + part_before[0][b];
+            start += (uint32_t)part_tot[0][b];
+        }
+        if (blockIdx.x == 0) {
+            for (int b = 0; b < kNumBins; ++b) hdr->bin_count[b] = (uint32_t)part_tot[0][b];
+            hdr->total_tiles = part_tot[0][kNumBins] + (part_tot[0][kNumBins + 1] << 32);
+        }
+    }
+    __syncthreads();
+
+    // Stable placement: rounds of kPlanBlock consecutive docs; inside a round, rank by
+    // (wave, lane) with one ballot per bin.
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const unsigned long long lanes_below = (1ull << lane) - 1ull;
+    const int64_t first = (int64_t)blockIdx.x * docs_per_block;
+    const int64_t last = first + docs_per_block < (int64_t)B ? first + docs_per_block : (int64_t)B;
+    for (int64_t base = first; base < last; base += kPlanBlock) {
+        const int64_t i = base + threadIdx.x;
+        const bool valid = i < last;
+        const int32_t len = valid ? lengths[i] : 0;
+        const uint32_t nt = tiles_of(len);
+        const int bin = valid ? bin_of(nt) : -1;
+        uint32_t rank = 0;
+        for (int b = 0; b < kNumBins; ++b) {
+            const unsigned long long m = __ballot(bin == b);
+            if (lane == 0) wave_cnt[wave][b] = (uint32_t)__popcll(m);
+            if (bin == b) rank = (uint32_t)__popcll(m & lanes_below);
+        }
+        __syncthreads();
+        if (valid) {
+            uint32_t slot = bin_next[bin] + rank;
+            for (int w = 0; w < wave; ++w) slot += wave_cnt[w][bin];
+            DocDesc dd;
+            dd.doc = (int32_t)i;
+            dd.offset = offsets[i];
+            dd.length = len > 0 ? len : 0;
+            dd.tiles = (int32_t)nt;
+            desc[slot] = dd;
+        }
+        __syncthreads();
+        if (threadIdx.x < kNumBins) {
+            uint32_t add = 0;
+            for (int w = 0; w < kPlanBlock / kWave; ++w) add += wave_cnt[w][threadIdx.x];
+            bin_next[threadIdx.x] += add;
+        }
+        __syncthreads();
+    }
+}
+
+__global__ void fill_kernel(float *__restrict__ out, int32_t n, float v)
+{
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+        out[i] = v;
+}
+
+// ---------------------------------------------------------------- device facts
+
+struct DeviceFacts {
+    int cus = 0;
+    int waves_per_cu = 0;  // most resident waves per CU
+    int status = MAXSIM_ERR_HIP;
+};
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_facts_once[kMaxDevices];
+DeviceFacts g_facts[kMaxDevices];
+
+int current_facts(DeviceFacts *out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MAXSIM_ERR_HIP;
+    std::call_once(g_facts_once[dev], [dev] {
+        DeviceFacts f;
+        int cus = 0, threads = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            hipDeviceGetAttribute(&threads, hipDeviceAttributeMaxThreadsPerMultiProcessor, dev) == hipSuccess &&
+            cus > 0 && threads >= kWave) {
+            f.cus = cus;
+            f.waves_per_cu = threads / kWave;
+            f.status = MAXSIM_OK;
+        }
+        g_facts[dev] = f;
+    });
+    *out = g_facts[dev];
+    return out->status;
+}
+
+// Per-kernel occupancy (resident score workgroups per CU), cached by kernel and LDS.
+struct OccEntry {
+    const void *fn;
+    int dev;
+    size_t lds;
+    int blocks;
+};
+std::mutex g_occ_mu;
+OccEntry g_occ[512];
+int g_occ_n = 0;
+
+int score_blocks_per_cu(const void *fn, size_t lds, int *blocks)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return MAXSIM_ERR_HIP;
+    std::lock_guard<std::mutex> lock(g_occ_mu);
+    for (int i = 0; i < g_occ_n; ++i)
+        if (g_occ[i].fn == fn && g_occ[i].dev == dev && g_occ[i].lds == lds) {
+            *blocks = g_occ[i].blocks;
+            return MAXSIM_OK;
+        }
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
+        return MAXSIM_ERR_HIP;
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, fn, kScoreBlock, lds) != hipSuccess || nb < 1)
+        return MAXSIM_ERR_HIP;
+    if (g_occ_n < (int)(sizeof(g_occ) / sizeof(g_occ[0]))) g_occ[g_occ_n++] = OccEntry{fn, dev, lds, nb};
+    *blocks = nb;
+    return MAXSIM_OK;
+}
+
+// ---------------------------------------------------------------- configuration
+
+struct Config {
+    int nks;      // K-steps of 32 columns: ceil(d / 32)
+    int nqt;      // query tiles per register group
+    int ngroups;  // register groups covering all query tiles
+    int lq_pad;   // ngroups * nqt * 16
+};
+
+Config choose_config(int32_t Lq, int32_t d)
+{
+    Config c;
+    c.nks = (d + kStepK - 1) / kStepK;
+    const int tiles = (Lq + kTileRows - 1) / kTileRows;
+    int max_nqt = kMaxFragsPerGroup / c.nks;
+    if (max_nqt > kMaxQTilesPerGroup) max_nqt = kMaxQTilesPerGroup;
+    if (tiles == 0) {
+        c.ngroups = 1;
+        c.nqt = 1;
+    } else {
+        c.ngroups = (tiles + max_nqt - 1) / max_nqt;
+        c.nqt = (tiles + c.ngroups - 1) / c.ngroups;
+    }
+    c.lq_pad = c.ngroups * c.nqt * kTileRows;
+    return c;
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_common(const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                 const int32_t *offsets, const int32_t *lengths, int32_t B, const float *scores)
+{
+    if (B < 0 || Lq < 0 || d < 1 || stride < d) return MAXSIM_ERR_INVALID_ARG;
+    if (B > 0 && (!docs || !offsets || !lengths || !scores)) return MAXSIM_ERR_INVALID_ARG;
+    if (B > 0 && Lq > 0 && !Q) return MAXSIM_ERR_INVALID_ARG;
+    if (d > kMaxD || d % 8 != 0 || Lq > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
+    if (stride % 8 != 0 || stride > kMaxStride) return MAXSIM_ERR_UNSUPPORTED;
+    if (B > 0 && !aligned16(docs)) return MAXSIM_ERR_UNSUPPORTED;
+    if (B > 0 && Lq > 0 && !aligned16(Q)) return MAXSIM_ERR_UNSUPPORTED;
+    if (B > 0 && (((uintptr_t)offsets | (uintptr_t)lengths | (uintptr_t)scores) & 3u))
+        return MAXSIM_ERR_INVALID_ARG;
+    return MAXSIM_OK;
+}
+
+int workspace_layout(int32_t Lq, int32_t d, int32_t B, Layout *L)
+{
+    DeviceFacts f;
+    if (current_facts(&f) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    const Config c = choose_config(Lq, d);
+    *L = make_layout(c.lq_pad, B, (uint32_t)(f.cus * f.waves_per_cu));
+    return MAXSIM_OK;
+}
+
+int launch_plan(const int32_t *offsets, const int32_t *lengths, int32_t B, const Layout &L,
+                char *ws, hipStream_t stream)
+{
+    uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
+    uint32_t *arrive = reinterpret_cast<uint32_t *>(ws + L.arrive);
+    Header *hdr = reinterpret_cast<Header *>(ws + L.header);
+    DocDesc *desc = reinterpret_cast<DocDesc *>(ws + L.desc);
+    hipLaunchKernelGGL(plan_count_kernel, dim3(L.plan_blocks), dim3(kPlanBlock), 0, stream,
+                       lengths, B, L.docs_per_plan_block, hist, arrive, L.arrive_slots, hdr);
+    if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_HIP;
+    hipLaunchKernelGGL(plan_scatter_kernel, dim3(L.plan_blocks), dim3(kPlanBlock), 0, stream,
+                       offsets, lengths, B, L.docs_per_plan_block, hist, L.plan_blocks, hdr, desc);
+    if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_HIP;
+    return MAXSIM_OK;
+}
+
+int launch_fill(float *scores, int32_t B, float v, hipStream_t stream)
+{
+    const int blocks = (B + 255) / 256 < 1024 ? (B + 255) / 256 : 1024;
+    hipLaunchKernelGGL(fill_kernel, dim3(blocks), dim3(256), 0, stream, scores, B, v);
+    return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
+}
+
+int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                 int32_t B, float *scores, const Layout &L, char *ws, hipStream_t stream)
+{
+    const Config c = choose_config(Lq, d);
+    if (c.lq_pad > kMaxLqPad || c.nqt * c.nks > kMaxFragsPerGroup) return MAXSIM_ERR_UNSUPPORTED;
+    const void *fn = dtype == MAXSIM_BF16 ? maxsim_score_kernel_bf16(c.nks, c.nqt)
+                                          : maxsim_score_kernel_f16(c.nks, c.nqt);
+    if (!fn) return MAXSIM_ERR_UNSUPPORTED;
+    const size_t lds = (size_t)c.lq_pad * (c.nks * kStepK + 8) * 2;
+    int per_cu = 0;
+    if (score_blocks_per_cu(fn, lds, &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    DeviceFacts f;
+    if (current_facts(&f) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    ScoreArgs a;
+    a.Q = static_cast<const uint16_t *>(Q);
+    a.docs = static_cast<const char *>(docs);
+    a.stride_bytes = stride * 2;
+    a.hdr = reinterpret_cast<const Header *>(ws + L.header);
+    a.desc = reinterpret_cast<const DocDesc *>(ws + L.desc);
+    a.claim = &reinterpret_cast<Header *>(ws + L.header)->claim;
+    a.arrive = reinterpret_cast<uint32_t *>(ws + L.arrive);
+    a.partials = reinterpret_cast<float *>(ws + L.partials);
+    a.scores = scores;
+    a.Lq = Lq;
+    a.d = d;
+    a.ngroups = c.ngroups;
+    a.lq_pad = c.lq_pad;
+    void *args[] = {&a};
+    const dim3 grid((unsigned)(f.cus * per_cu));
+    if (hipLaunchKernel(fn, grid, dim3(kScoreBlock), args, lds, stream) != hipSuccess) return MAXSIM_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
+}
+
+int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+           const int32_t *offsets, const int32_t *lengths, int32_t B, float *scores, void *stream_ptr)
+{
+    const int st = check_common(Q, Lq, d, docs, stride, offsets, lengths, B, scores);
+    if (st != MAXSIM_OK) return st;
+    if (B == 0) return MAXSIM_OK;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    if (Lq == 0) return launch_fill(scores, B, 0.0f, stream);
+    Layout L;
+    if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    void *ws = nullptr;
+    if (hipMallocAsync(&ws, L.total, stream) != hipSuccess) return MAXSIM_ERR_HIP;
+    int rc = launch_plan(offsets, lengths, B, L, static_cast<char *>(ws), stream);
+    if (rc == MAXSIM_OK)
+        rc = launch_score(dtype, Q, Lq, d, docs, stride, B, scores, L, static_cast<char *>(ws), stream);
+    if (hipFreeAsync(ws, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
+    return rc;
+}
+
+}  // namespace
+
+extern "C" {
+
+int maxsim_rerank(const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                  const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, float *scores,
+                  void *stream)
+{
+    return rerank(MAXSIM_F16, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores, stream);
+}
+
+int maxsim_rerank_bf16(const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                       const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                       float *scores, void *stream)
+{
+    return rerank(MAXSIM_BF16, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores, stream);
+}
+
+const char *maxsim_status_string(int status)
+{
+    switch (status) {
+    case MAXSIM_OK: return "ok";
+    case MAXSIM_ERR_INVALID_ARG: return "invalid argument (null pointer, negative size, stride < d or bad format)";
+    case MAXSIM_ERR_UNSUPPORTED: return "unsupported shape or alignment (need d <= 256 and d % 8 == 0, Lq <= 256, stride % 8 == 0 and <= 2^24, 16-byte aligned Q and docs)";
+    case MAXSIM_ERR_HIP: return "HIP call failed (no device, allocation or launch failure)";
+    case MAXSIM_ERR_WORKSPACE: return "workspace null, not 256-byte aligned, or too small";
+    default: return "unknown status";
+    }
+}
+
+int maxsim_workspace_size(int32_t Lq, int32_t d, int32_t B, size_t *bytes)
+{
+    if (!bytes || B < 0 || Lq < 0 || d < 1) return MAXSIM_ERR_INVALID_ARG;
+    if (d > kMaxD || d % 8 != 0 || Lq > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
+    Layout L;
+    if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    *bytes = L.total;
+    return MAXSIM_OK;
+}
+
+int maxsim_plan(const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, int32_t Lq,
+                int32_t d, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (B < 0 || Lq < 0 || d < 1) return MAXSIM_ERR_INVALID_ARG;
+    if (B > 0 && (!doc_offsets || !doc_lengths)) return MAXSIM_ERR_INVALID_ARG;
+    if (d > kMaxD || d % 8 != 0 || Lq > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
+    if (B == 0 || Lq == 0) return MAXSIM_OK;
+    if (!workspace || ((uintptr_t)workspace & 255u)) return MAXSIM_ERR_WORKSPACE;
+    Layout L;
+    if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
+    return launch_plan(doc_offsets, doc_lengths, B, L, static_cast<char *>(workspace),
+                       static_cast<hipStream_t>(stream));
+}
+
+int maxsim_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                 const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, float *scores,
+                 void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
+    const int st = check_common(Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores);
+    if (st != MAXSIM_OK) return st;
+    if (B == 0) return MAXSIM_OK;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (Lq == 0) return launch_fill(scores, B, 0.0f, s);
+    if (!workspace || ((uintptr_t)workspace & 255u)) return MAXSIM_ERR_WORKSPACE;
+    Layout L;
+    if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
+    return launch_score(dtype, Q, Lq, d, docs, stride, B, scores, L, static_cast<char *>(workspace), s);
+}
+
+int maxsim_version(void) { return 100; }
+
+}  // extern "C"

@@ -1,0 +1,52 @@
+// Score kernel instances for one element format and one K-step count, chosen by
+// -DMAXSIM_BF16=0|1 -DMAXSIM_NKS=1..8 (the build compiles this file once per pair, in
+// parallel). Query tiles per group NQT run 1..8 with NQT * NKS <= 32.
+#include "maxsim_score.h"
+
+#ifndef MAXSIM_BF16
+#error "define MAXSIM_BF16"
+#endif
+#ifndef MAXSIM_NKS
+#error "define MAXSIM_NKS"
+#endif
+
+namespace {
+
+constexpr int NKS = MAXSIM_NKS;
+constexpr bool BF = MAXSIM_BF16 != 0;
+// Pipeline depth in doc tiles: 8-12 KB of loads outstanding per wave.
+constexpr int P = NKS >= 5 ? 2 : (NKS >= 3 ? 3 : (NKS == 2 ? 5 : 8));
+
+template <int NQT>
+const void *entry()
+{
+    if constexpr (NQT * NKS <= maxsim::kMaxFragsPerGroup)
+        return reinterpret_cast<const void *>(&maxsim::score_kernel<NKS, NQT, BF, P>);
+    else
+        return nullptr;
+}
+
+}  // namespace
+
+#define MAXSIM_CAT2(a, b) a##b
+#define MAXSIM_CAT(a, b) MAXSIM_CAT2(a, b)
+#if MAXSIM_BF16
+#define MAXSIM_LOOKUP MAXSIM_CAT(maxsim_score_kernel_bf16_k, MAXSIM_NKS)
+#else
+#define MAXSIM_LOOKUP MAXSIM_CAT(maxsim_score_kernel_f16_k, MAXSIM_NKS)
+#endif
+
+const void *MAXSIM_LOOKUP(int nqt)
+{
+    switch (nqt) {
+    case 1: return entry<1>();
+    case 2: return entry<2>();
+    case 3: return entry<3>();
+    case 4: return entry<4>();
+    case 5: return entry<5>();
+    case 6: return entry<6>();
+    case 7: return entry<7>();
+    case 8: return entry<8>();
+    default: return nullptr;
+    }
+}

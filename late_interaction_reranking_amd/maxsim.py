@@ -1,0 +1,209 @@
+"""Python binding of libmaxsim.so (ctypes). Argument marshalling only: every step of
+the computation runs in the library's HIP kernels; PyTorch supplies device memory and
+the current stream.
+
+The functions carry the C ABI's names (include/maxsim.h) and take torch tensors:
+
+    maxsim_rerank(Q, docs, doc_offsets, doc_lengths)       fp16 Q and docs
+    maxsim_rerank_bf16(Q, docs, doc_offsets, doc_lengths)  bf16 Q and docs
+    maxsim_workspace_size(Lq, d, B) -> bytes
+    maxsim_plan(doc_offsets, doc_lengths, Lq, d, workspace)
+    maxsim_score(Q, docs, doc_offsets, doc_lengths, workspace, scores=None)
+    rerank(...)  picks maxsim_rerank or maxsim_rerank_bf16 from Q's dtype
+
+Q is [Lq, d] and contiguous; docs is a 2-D view whose rows are docs.stride(0) elements
+apart with unit column stride (a column slice of a wider tensor works: its extra
+columns are never read); doc_offsets and doc_lengths are int32 [B] on the same device.
+The scores are fp32 [B] (Flash-MaxSim rerank page, docs.vllm.ai,
+vllm.v1.pool.flash_maxsim.flash_maxsim_rerank, `flash_maxsim_rerank_direct`).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+__all__ = [
+    "MaxSimError",
+    "library_path",
+    "load",
+    "maxsim_rerank",
+    "maxsim_rerank_bf16",
+    "maxsim_status_string",
+    "maxsim_workspace_size",
+    "maxsim_plan",
+    "maxsim_score",
+    "maxsim_version",
+    "rerank",
+    "MAXSIM_F16",
+    "MAXSIM_BF16",
+]
+
+MAXSIM_OK = 0
+MAXSIM_F16 = 0
+MAXSIM_BF16 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_lock = threading.Lock()
+_lib = None
+
+
+class MaxSimError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: status {status}: {maxsim_status_string(status)}")
+
+
+def library_path() -> str:
+    return os.path.join(_HERE, "libmaxsim.so")
+
+
+def load() -> ctypes.CDLL:
+    """Load libmaxsim.so (built in-tree by late_interaction_reranking_amd.build)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        path = library_path()
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m late_interaction_reranking_amd.build`"
+            )
+        lib = ctypes.CDLL(path)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        rr = [P, I32, I32, P, I64, P, P, I32, P, P]
+        for name in ("maxsim_rerank", "maxsim_rerank_bf16"):
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = rr
+        lib.maxsim_status_string.restype = ctypes.c_char_p
+        lib.maxsim_status_string.argtypes = [ctypes.c_int]
+        lib.maxsim_workspace_size.restype = ctypes.c_int
+        lib.maxsim_workspace_size.argtypes = [I32, I32, I32, ctypes.POINTER(SZ)]
+        lib.maxsim_plan.restype = ctypes.c_int
+        lib.maxsim_plan.argtypes = [P, P, I32, I32, I32, P, SZ, P]
+        lib.maxsim_score.restype = ctypes.c_int
+        lib.maxsim_score.argtypes = [ctypes.c_int, P, I32, I32, P, I64, P, P, I32, P, P, SZ, P]
+        lib.maxsim_version.restype = ctypes.c_int
+        lib.maxsim_version.argtypes = []
+        _lib = lib
+        return lib
+
+
+def maxsim_status_string(status: int) -> str:
+    return load().maxsim_status_string(int(status)).decode()
+
+
+def maxsim_version() -> int:
+    return int(load().maxsim_version())
+
+
+def _check(status: int, where: str) -> None:
+    if status != MAXSIM_OK:
+        raise MaxSimError(status, where)
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _marshal(Q, docs, doc_offsets, doc_lengths, dtype):
+    if Q.dim() != 2 or docs.dim() != 2:
+        raise ValueError("Q and docs must be 2-D")
+    if Q.dtype != dtype or docs.dtype != dtype:
+        raise TypeError(f"Q and docs must both be {dtype}")
+    if doc_offsets.dtype != torch.int32 or doc_lengths.dtype != torch.int32:
+        raise TypeError("doc_offsets and doc_lengths must be int32")
+    if doc_offsets.dim() != 1 or doc_offsets.shape != doc_lengths.shape:
+        raise ValueError("doc_offsets and doc_lengths must be 1-D of equal length")
+    dev = docs.device
+    for name, t in (("Q", Q), ("docs", docs), ("doc_offsets", doc_offsets), ("doc_lengths", doc_lengths)):
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError(f"{name} must live on the GPU, with docs")
+    if not Q.is_contiguous() or not doc_offsets.is_contiguous() or not doc_lengths.is_contiguous():
+        raise ValueError("Q, doc_offsets and doc_lengths must be contiguous")
+    if docs.shape[0] > 0 and docs.stride(1) != 1:
+        raise ValueError("docs must have unit column stride")
+    if Q.shape[1] != docs.shape[1]:
+        raise ValueError("Q and docs must have the same width d")
+    Lq, d = int(Q.shape[0]), int(Q.shape[1])
+    stride = int(docs.stride(0)) if docs.shape[0] > 1 else max(int(docs.stride(0)), d)
+    return Lq, d, stride, int(doc_offsets.shape[0])
+
+
+def _rerank(fn_name, dtype, Q, docs, doc_offsets, doc_lengths, scores=None):
+    Lq, d, stride, B = _marshal(Q, docs, doc_offsets, doc_lengths, dtype)
+    if scores is None:
+        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
+    elif scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    with torch.cuda.device(docs.device):
+        st = getattr(load(), fn_name)(
+            Q.data_ptr(), Lq, d, docs.data_ptr(), stride, doc_offsets.data_ptr(),
+            doc_lengths.data_ptr(), B, scores.data_ptr(), _stream(docs),
+        )
+    _check(st, fn_name)
+    return scores
+
+
+def maxsim_rerank(Q, docs, doc_offsets, doc_lengths, scores=None) -> torch.Tensor:
+    """fp32 [B] MaxSim scores, fp16 inputs."""
+    return _rerank("maxsim_rerank", torch.float16, Q, docs, doc_offsets, doc_lengths, scores)
+
+
+def maxsim_rerank_bf16(Q, docs, doc_offsets, doc_lengths, scores=None) -> torch.Tensor:
+    """fp32 [B] MaxSim scores, bf16 inputs."""
+    return _rerank("maxsim_rerank_bf16", torch.bfloat16, Q, docs, doc_offsets, doc_lengths, scores)
+
+
+def rerank(Q, docs, doc_offsets, doc_lengths, scores=None) -> torch.Tensor:
+    """maxsim_rerank or maxsim_rerank_bf16, chosen by Q's dtype."""
+    if Q.dtype == torch.bfloat16:
+        return maxsim_rerank_bf16(Q, docs, doc_offsets, doc_lengths, scores)
+    return maxsim_rerank(Q, docs, doc_offsets, doc_lengths, scores)
+
+
+def maxsim_workspace_size(Lq: int, d: int, B: int, device=None) -> int:
+    """Bytes of workspace maxsim_plan / maxsim_score need on `device` (current by default)."""
+    n = ctypes.c_size_t(0)
+    dev = torch.device("cuda") if device is None else torch.device(device)
+    with torch.cuda.device(dev):
+        st = load().maxsim_workspace_size(int(Lq), int(d), int(B), ctypes.byref(n))
+    _check(st, "maxsim_workspace_size")
+    return int(n.value)
+
+
+def _ws(workspace: torch.Tensor) -> tuple[int, int]:
+    if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device.type != "cuda":
+        raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    return workspace.data_ptr(), int(workspace.numel())
+
+
+def maxsim_plan(doc_offsets, doc_lengths, Lq: int, d: int, workspace: torch.Tensor) -> None:
+    """Enqueue the length-binned schedule into `workspace` on the current stream."""
+    if doc_offsets.dtype != torch.int32 or doc_lengths.dtype != torch.int32:
+        raise TypeError("doc_offsets and doc_lengths must be int32")
+    ptr, nbytes = _ws(workspace)
+    with torch.cuda.device(workspace.device):
+        st = load().maxsim_plan(doc_offsets.data_ptr(), doc_lengths.data_ptr(), int(doc_offsets.shape[0]),
+                                int(Lq), int(d), ptr, nbytes, _stream(workspace))
+    _check(st, "maxsim_plan")
+
+
+def maxsim_score(Q, docs, doc_offsets, doc_lengths, workspace: torch.Tensor, scores=None) -> torch.Tensor:
+    """Enqueue the score kernel over a schedule maxsim_plan wrote into `workspace`."""
+    dtype = torch.bfloat16 if Q.dtype == torch.bfloat16 else torch.float16
+    Lq, d, stride, B = _marshal(Q, docs, doc_offsets, doc_lengths, dtype)
+    if scores is None:
+        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
+    ptr, nbytes = _ws(workspace)
+    code = MAXSIM_BF16 if dtype == torch.bfloat16 else MAXSIM_F16
+    with torch.cuda.device(docs.device):
+        st = load().maxsim_score(code, Q.data_ptr(), Lq, d, docs.data_ptr(), stride,
+                                 doc_offsets.data_ptr(), doc_lengths.data_ptr(), B,
+                                 scores.data_ptr(), ptr, nbytes, _stream(docs))
+    _check(st, "maxsim_score")
+    return scores

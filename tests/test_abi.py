@@ -1,0 +1,111 @@
+"""The C-ABI library without a GPU: it loads, exports every declared symbol, and rejects
+bad arguments on the host before any HIP call."""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import late_interaction_reranking_amd as lir
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "maxsim.h")
+
+OK, INVALID, UNSUPPORTED, HIP, WORKSPACE = 0, 1, 2, 3, 4
+
+
+def declared_functions() -> list[str]:
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"MAXSIM_API\s+[\w\s\*]*?\b(maxsim_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return lir.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for n in ("maxsim_rerank", "maxsim_rerank_bf16", "maxsim_status_string",
+              "maxsim_workspace_size", "maxsim_plan", "maxsim_score", "maxsim_version"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_only_declared_symbols_are_exported():
+    import subprocess
+
+    out = subprocess.run(["nm", "-D", "--defined-only", lir.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = sorted({ln.split()[-1] for ln in out.splitlines() if " T " in ln})
+    assert exported == declared_functions()
+
+
+def test_status_strings(lib):
+    for code in (OK, INVALID, UNSUPPORTED, HIP, WORKSPACE, 99, -1):
+        s = lir.maxsim_status_string(code)
+        assert isinstance(s, str) and s
+    assert lir.maxsim_status_string(99) == "unknown status"
+    assert lir.maxsim_version() == 100
+
+
+FAKE = 0x7F0000000000  # 256-byte aligned stand-in for a device address; never dereferenced
+
+
+def call(lib, fn="maxsim_rerank", Q=FAKE, Lq=32, d=128, docs=FAKE, stride=128, offs=FAKE,
+         lens=FAKE + 1024, B=10, scores=FAKE + 4096):
+    return getattr(lib, fn)(Q, Lq, d, docs, stride, offs, lens, B, scores, None)
+
+
+@pytest.mark.parametrize("fn", ["maxsim_rerank", "maxsim_rerank_bf16"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(B=-1), INVALID),
+    (dict(Lq=-1), INVALID),
+    (dict(d=0), INVALID),
+    (dict(stride=64), INVALID),          # stride < d
+    (dict(docs=None), INVALID),
+    (dict(offs=None), INVALID),
+    (dict(lens=None), INVALID),
+    (dict(scores=None), INVALID),
+    (dict(Q=None), INVALID),
+    (dict(d=12, stride=16), UNSUPPORTED),   # d % 8
+    (dict(d=264, stride=264), UNSUPPORTED),  # d > 256
+    (dict(Lq=257), UNSUPPORTED),
+    (dict(stride=132), UNSUPPORTED),         # stride % 8
+    (dict(stride=(1 << 24) + 8), UNSUPPORTED),
+    (dict(docs=FAKE + 8), UNSUPPORTED),      # docs not 16-byte aligned
+    (dict(Q=FAKE + 4), UNSUPPORTED),         # Q not 16-byte aligned
+    (dict(offs=FAKE + 2), INVALID),          # int32 arrays not 4-byte aligned
+    (dict(scores=FAKE + 2), INVALID),
+    (dict(B=0, docs=None, offs=None, lens=None, scores=None), OK),  # nothing to do
+])
+def test_host_validation(lib, fn, kw, code):
+    assert call(lib, fn, **kw) == code
+
+
+def test_staged_validation(lib):
+    P = ctypes.c_void_p
+    # unknown element format
+    assert lib.maxsim_score(7, FAKE, 32, 128, FAKE, 128, FAKE, FAKE, 4, FAKE, FAKE, 1 << 20, None) == INVALID
+    # workspace missing / misaligned (checked before the device is touched)
+    assert lib.maxsim_score(0, FAKE, 32, 128, FAKE, 128, FAKE, FAKE, 4, FAKE, None, 1 << 20, None) == WORKSPACE
+    assert lib.maxsim_score(0, FAKE, 32, 128, FAKE, 128, FAKE, FAKE, 4, FAKE, FAKE + 16, 1 << 20, None) == WORKSPACE
+    assert lib.maxsim_plan(FAKE, FAKE, 4, 32, 128, None, 1 << 20, None) == WORKSPACE
+    assert lib.maxsim_plan(FAKE, FAKE, 4, 32, 128, FAKE + 64, 1 << 20, None) == WORKSPACE
+    assert lib.maxsim_plan(None, FAKE, 4, 32, 128, FAKE, 1 << 20, None) == INVALID
+    assert lib.maxsim_plan(FAKE, FAKE, -2, 32, 128, FAKE, 1 << 20, None) == INVALID
+    assert lib.maxsim_plan(FAKE, FAKE, 4, 32, 100, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert lib.maxsim_plan(FAKE, FAKE, 0, 32, 128, None, 0, None) == OK
+    n = ctypes.c_size_t(0)
+    assert lib.maxsim_workspace_size(32, 128, -1, ctypes.byref(n)) == INVALID
+    assert lib.maxsim_workspace_size(32, 128, 10, None) == INVALID
+    assert lib.maxsim_workspace_size(32, 100, 10, ctypes.byref(n)) == UNSUPPORTED
+    del P
