@@ -35,8 +35,6 @@ constexpr int kMinChunkTiles = 2;
 
 struct Header {
     unsigned long long total_tiles;          // sum over docs of ceil(len / 16)
-    uint32_t claim;                          // next work item (score kernel's counter)
-    uint32_t reserved;
     uint32_t bin_count[kNumBins];            // docs per bin
 };
 
@@ -55,9 +53,9 @@ __host__ __device__ inline int bin_of(uint32_t nt)
 __host__ __device__ inline size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
 struct Layout {
-    size_t header, hist, arrive, partials, desc, total;
+    size_t header, hist, partials, desc, total;
     uint32_t plan_blocks, docs_per_plan_block;
-    uint32_t arrive_slots, partial_slots;
+    uint32_t partial_slots;
     int lq_pad;
 };
 
@@ -65,8 +63,8 @@ struct Layout {
 // split doc has nt > 2^(b-1) >= CT / 2 tiles: there are fewer than 2 T / CT of them,
 // and, since CT >= T / (kItemsPerWave * W), fewer than 2 * kItemsPerWave * W. Each gets
 // ceil(2^b / CT) < 2 nt / CT + 1 chunks, fewer than 4 * kItemsPerWave * W in all.
-// Split docs come first in both the desc order and the claim order (their bins are
-// the highest), so the first desc / claim indices serve as their slots.
+// Split docs come first in the claim order (their bins are the highest), so a split
+// chunk's claim index serves as its slot of per-row maxima.
 inline Layout make_layout(int lq_pad, int32_t B, uint32_t waves_max)
 {
     Layout L{};
@@ -74,13 +72,11 @@ inline Layout make_layout(int lq_pad, int32_t B, uint32_t waves_max)
     while ((uint64_t)rounds * kPlanBlock * kPlanMaxBlocks < (uint64_t)(B > 0 ? B : 0)) rounds *= 2;
     L.docs_per_plan_block = rounds * kPlanBlock;
     L.plan_blocks = B > 0 ? (uint32_t)(((uint64_t)B + L.docs_per_plan_block - 1) / L.docs_per_plan_block) : 1;
-    L.arrive_slots = 2u * kItemsPerWave * waves_max;
     L.partial_slots = 4u * kItemsPerWave * waves_max;
     L.lq_pad = lq_pad;
     size_t off = 0;
     L.header = off;   off = align256(off + sizeof(Header));
     L.hist = off;     off = align256(off + (size_t)L.plan_blocks * kHistStride * 4);
-    L.arrive = off;   off = align256(off + (size_t)L.arrive_slots * 4);
     L.partials = off; off = align256(off + (size_t)L.partial_slots * (size_t)lq_pad * 4);
     L.desc = off;     off = align256(off + (size_t)(B > 0 ? B : 0) * sizeof(DocDesc));
     L.total = off;
@@ -94,11 +90,19 @@ struct ScoreArgs {
     int64_t stride_bytes;
     const Header *hdr;
     const DocDesc *desc;
-    uint32_t *claim;
-    uint32_t *arrive;
     float *partials;          // [partial_slots, lq_pad]
     float *scores;
     int32_t Lq, d, ngroups, lq_pad;
+};
+
+// ---------------------------------------------------------------- combine kernel
+struct CombineArgs {
+    const Header *hdr;
+    const DocDesc *desc;
+    const float *partials;
+    float *scores;
+    uint32_t score_waves;     // W of the score launch (fixes the chunking)
+    int32_t Lq, nqt, ngroups, lq_pad;
 };
 
 }  // namespace maxsim

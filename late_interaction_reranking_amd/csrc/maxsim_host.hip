@@ -5,6 +5,7 @@
 #include <mutex>
 
 #include "maxsim_common.h"
+#include "maxsim_sched.h"
 
 using namespace maxsim;
 
@@ -45,7 +46,7 @@ namespace {
 // docs start first and the short ones fill in the tail.
 //
 // Pass 1 (count) writes, per plan block, the number of its docs in each bin and the
-// sum of their tile counts; it also zeroes the score kernel's counters. Pass 2
+// sum of their tile counts. Pass 2
 // (scatter) sums those rows to get each bin's start and the block's place inside it,
 // then writes every doc's descriptor at its slot. Block 0 of pass 2 also writes the
 // bin totals and the total tile count to the header.
@@ -57,8 +58,7 @@ __device__ __forceinline__ uint32_t tiles_of(int32_t len)
 
 __global__ void __launch_bounds__(kPlanBlock)
 plan_count_kernel(const int32_t *__restrict__ lengths, int32_t B, uint32_t docs_per_block,
-                  uint32_t *__restrict__ hist, uint32_t *__restrict__ arrive, uint32_t n_arrive,
-                  Header *__restrict__ hdr)
+                  uint32_t *__restrict__ hist)
 {
     __shared__ uint32_t cnt[kNumBins];
     __shared__ unsigned long long tiles;
@@ -82,10 +82,6 @@ plan_count_kernel(const int32_t *__restrict__ lengths, int32_t B, uint32_t docs_
     if (threadIdx.x < kNumBins) row[threadIdx.x] = cnt[threadIdx.x];
     if (threadIdx.x == kNumBins) row[kNumBins] = (uint32_t)tiles;
     if (threadIdx.x == kNumBins + 1) row[kNumBins + 1] = (uint32_t)(tiles >> 32);
-
-    for (uint32_t e = blockIdx.x * kPlanBlock + threadIdx.x; e < n_arrive; e += gridDim.x * kPlanBlock)
-        arrive[e] = 0;
-    if (blockIdx.x == 0 && threadIdx.x == 0) hdr->claim = 0;
 }
 
 __global__ void __launch_bounds__(kPlanBlock)
@@ -176,6 +172,52 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
             bin_next[threadIdx.x] += add;
         }
         __syncthreads();
+    }
+}
+
+// Split docs: max over each doc's chunk slots, then the score kernel's fixed-order sum
+// (lane l adds, per query tile, rows 4 (l / 16) + 0..3; then lanes 0, 16, 32, 48), so a
+// split doc's score is bitwise the one it would get unsplit. One wave per doc.
+__global__ void __launch_bounds__(kScoreBlock)
+combine_kernel(const CombineArgs a)
+{
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    __shared__ BinTables tab;
+    __shared__ float s_comb[kScoreWaves][kMaxLqPad];
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    if (threadIdx.x == 0) fill_bin_tables(a.hdr, a.score_waves, tab);
+    __syncthreads();
+    const LaneBins L = lane_bins(tab, lane);
+    const uint32_t split = tab.split_docs;
+    const int kgroup = lane >> 4;
+    float *mx = s_comb[wave];
+    for (uint32_t di = blockIdx.x * kScoreWaves + wave; di < split; di += gridDim.x * kScoreWaves) {
+        const Item it = locate_doc(L, lane, di);
+        for (int q = lane; q < a.lq_pad; q += kWave) {
+            float m = NEG_INF;
+            for (uint32_t k = 0; k < it.K; ++k) {
+                const float v = a.partials[(size_t)(it.first + k) * a.lq_pad + q];
+                m = v > m ? v : m;
+            }
+            mx[q] = m;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float lane_sum = 0.0f;
+        for (int grp = 0; grp < a.ngroups; ++grp)
+            for (int qt = 0; qt < a.nqt; ++qt)
+                for (int i = 0; i < 4; ++i) {
+                    const int q = (grp * a.nqt + qt) * kTileRows + kgroup * 4 + i;
+                    lane_sum += q < a.Lq ? mx[q] : 0.0f;
+                }
+        __builtin_amdgcn_wave_barrier();
+        const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 0));
+        const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 16));
+        const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 32));
+        const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 48));
+        if (lane == 0) a.scores[a.desc[di].doc] = ((s0 + s1) + s2) + s3;
     }
 }
 
@@ -306,11 +348,10 @@ int launch_plan(const int32_t *offsets, const int32_t *lengths, int32_t B, const
                 char *ws, hipStream_t stream)
 {
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
-    uint32_t *arrive = reinterpret_cast<uint32_t *>(ws + L.arrive);
     Header *hdr = reinterpret_cast<Header *>(ws + L.header);
     DocDesc *desc = reinterpret_cast<DocDesc *>(ws + L.desc);
     hipLaunchKernelGGL(plan_count_kernel, dim3(L.plan_blocks), dim3(kPlanBlock), 0, stream,
-                       lengths, B, L.docs_per_plan_block, hist, arrive, L.arrive_slots, hdr);
+                       lengths, B, L.docs_per_plan_block, hist);
     if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_HIP;
     hipLaunchKernelGGL(plan_scatter_kernel, dim3(L.plan_blocks), dim3(kPlanBlock), 0, stream,
                        offsets, lengths, B, L.docs_per_plan_block, hist, L.plan_blocks, hdr, desc);
@@ -344,8 +385,6 @@ int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     a.stride_bytes = stride * 2;
     a.hdr = reinterpret_cast<const Header *>(ws + L.header);
     a.desc = reinterpret_cast<const DocDesc *>(ws + L.desc);
-    a.claim = &reinterpret_cast<Header *>(ws + L.header)->claim;
-    a.arrive = reinterpret_cast<uint32_t *>(ws + L.arrive);
     a.partials = reinterpret_cast<float *>(ws + L.partials);
     a.scores = scores;
     a.Lq = Lq;
@@ -355,6 +394,19 @@ int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     void *args[] = {&a};
     const dim3 grid((unsigned)(f.cus * per_cu));
     if (hipLaunchKernel(fn, grid, dim3(kScoreBlock), args, lds, stream) != hipSuccess) return MAXSIM_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_HIP;
+
+    CombineArgs ca;
+    ca.hdr = a.hdr;
+    ca.desc = a.desc;
+    ca.partials = a.partials;
+    ca.scores = scores;
+    ca.score_waves = grid.x * kScoreWaves;
+    ca.Lq = Lq;
+    ca.nqt = c.nqt;
+    ca.ngroups = c.ngroups;
+    ca.lq_pad = c.lq_pad;
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)f.cus), dim3(kScoreBlock), 0, stream, ca);
     return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
 }
 

@@ -1,0 +1,105 @@
+// Work-item arithmetic of the length-binned schedule, shared by the score kernel and
+// the combine kernel (device side).
+//
+// The plan kernels leave, in the workspace header, the number of docs in each tile-count
+// bin and the total tile count T; the doc descriptors sit in `desc`, bins in descending
+// order. A kernel turns that into work items:
+//   - chunk size CT = max(2, ceil(T / (kItemsPerWave * W))) tiles, W = score waves;
+//   - a doc of bin b is cut into K_b = ceil(2^b / CT) chunks when 2^b > CT (else 1);
+//     chunk c covers its tiles [c nt / K_b, (c + 1) nt / K_b), never empty since
+//     nt > 2^(b-1) >= K_b;
+//   - claims (work items) run bin 27 first ... bin 0 last, a doc's chunks adjacent.
+#pragma once
+
+#include "maxsim_common.h"
+
+namespace maxsim {
+
+struct BinTables {
+    uint32_t claim_end[kNumBins];   // claims of bins >= b
+    uint32_t desc_start[kNumBins];  // first desc index of bin b
+    uint32_t chunks[kNumBins];      // K_b
+    uint32_t total_claims;
+    uint32_t split_docs;            // docs with K_b > 1: desc indices [0, split_docs)
+};
+
+// One thread fills the tables; the caller publishes them with a barrier.
+__device__ inline void fill_bin_tables(const Header *hdr, uint32_t waves, BinTables &t)
+{
+    const unsigned long long T = hdr->total_tiles;
+    const unsigned long long per = (unsigned long long)waves * kItemsPerWave;
+    unsigned long long ct = (T + per - 1) / per;
+    if (ct < kMinChunkTiles) ct = kMinChunkTiles;
+    if (ct > (1ull << 28)) ct = 1ull << 28;  // above every bin's 2^b: no splits
+    const uint32_t ct32 = (uint32_t)ct;
+    uint32_t claims = 0, descs = 0, split = 0;
+    for (int b = kNumBins - 1; b >= 0; --b) {
+        const uint32_t cnt = hdr->bin_count[b];
+        const uint32_t cap = 1u << b;  // most tiles a doc of bin b has
+        const uint32_t K = cap > ct32 ? (cap + ct32 - 1u) / ct32 : 1u;
+        t.desc_start[b] = descs;
+        t.chunks[b] = K;
+        if (K > 1) split += cnt;
+        descs += cnt;
+        claims += cnt * K;
+        t.claim_end[b] = claims;
+    }
+    t.total_claims = claims;
+    t.split_docs = split;
+}
+
+// Per-lane copy of the tables (lane b < kNumBins holds bin b) for ballot searches.
+struct LaneBins {
+    uint32_t claim_end, desc_start, chunks;
+};
+
+__device__ inline LaneBins lane_bins(const BinTables &t, int lane)
+{
+    LaneBins L;
+    L.claim_end = lane < kNumBins ? t.claim_end[lane] : 0u;
+    L.desc_start = lane < kNumBins ? t.desc_start[lane] : 0xFFFFFFFFu;
+    L.chunks = lane < kNumBins ? t.chunks[lane] : 1u;
+    return L;
+}
+
+struct Item {
+    uint32_t di;     // desc index of the doc
+    uint32_t c;      // chunk of the doc
+    uint32_t K;      // chunks of the doc
+    uint32_t first;  // claim index of the doc's chunk 0
+};
+
+// Work item of claim g (< total claims). g < claim_end[b] holds exactly for
+// b <= bin(g), so the bin is the highest set bit of the ballot.
+__device__ inline Item locate_claim(const LaneBins &L, int lane, uint32_t g)
+{
+    const unsigned long long below = __ballot(lane < kNumBins && g < L.claim_end);
+    const int b = 63 - __builtin_clzll(below);
+    const uint32_t begin = b + 1 < kNumBins ? __builtin_amdgcn_readlane(L.claim_end, b + 1) : 0u;
+    Item it;
+    it.K = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(L.chunks, b));
+    const uint32_t local = g - __builtin_amdgcn_readfirstlane(begin);
+    const uint32_t j = local / it.K;
+    it.c = local - j * it.K;
+    it.di = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(L.desc_start, b)) + j;
+    it.first = g - it.c;
+    return it;
+}
+
+// Work items of the doc at desc index di. di >= desc_start[b] holds exactly for
+// b >= bin(di), so the bin is the lowest set bit of the ballot.
+__device__ inline Item locate_doc(const LaneBins &L, int lane, uint32_t di)
+{
+    const unsigned long long above = __ballot(lane < kNumBins && di >= L.desc_start);
+    const int b = __builtin_ctzll(above);
+    const uint32_t begin = b + 1 < kNumBins ? __builtin_amdgcn_readlane(L.claim_end, b + 1) : 0u;
+    Item it;
+    it.K = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(L.chunks, b));
+    const uint32_t j = di - __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(L.desc_start, b));
+    it.di = di;
+    it.c = 0;
+    it.first = __builtin_amdgcn_readfirstlane(begin) + j * it.K;
+    return it;
+}
+
+}  // namespace maxsim

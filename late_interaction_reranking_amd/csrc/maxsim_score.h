@@ -7,10 +7,13 @@
 // rows t of Q[q] . X[off_i + t], fp16/bf16 inputs, fp32 products and sums.
 //
 // Mapping onto the hardware:
-//   - Persistent workgroups of 4 waves, as many as fit on every CU. Each wave claims
-//     work items (a doc, or a chunk of a long doc's tiles) from the length-binned
-//     schedule that the plan kernels wrote, longest bins first, through one atomic
-//     counter.
+//   - Persistent workgroups of 4 waves, as many as fit on every CU. The work items (a
+//     doc, or a chunk of a long doc's tiles) of the length-binned schedule that the
+//     plan kernels wrote, longest bins first, are dealt to the W waves in rounds, in
+//     alternating direction (round r gives item r W + w to wave w, or to wave W-1-w
+//     when r is odd), so every wave gets a similar mix of long and short items. No
+//     atomics: a shared claim counter serialises across the chip's eight XCDs.
+//     Each wave loads the descriptor of its next item while it scores the current one.
 //   - Q is staged once per workgroup into LDS, zero-padded to 16-row tiles and
 //     32-column K-steps. Each wave keeps its MFMA A-fragments of one group of up to
 //     NQT query tiles in registers; with one group (every Lq * d that fits 128 VGPRs)
@@ -33,12 +36,15 @@
 //     summed in one fixed order (ascending query tile, then j, then the four lane
 //     groups), whether the doc was scored in one item or several, so scores do not
 //     depend on how the schedule chunked the doc.
-//   - A doc split into K chunks: each chunk writes its per-row maxima to its own slot,
-//     bumps the doc's arrival counter, and the chunk that arrives last takes the max
-//     over the K slots (exact, so order-free) and does the fixed-order sum.
+//   - A doc split into K chunks: each chunk writes its per-row maxima to its own slot
+//     with plain stores; the combine kernel, launched next on the same stream, takes
+//     the max over the K slots (exact, so order-free) and does the same fixed-order
+//     sum. The kernel boundary is the only synchronisation: no fences in the hot loop
+//     (on this chip a device-scope fence writes back and invalidates the XCD's L2).
 #pragma once
 
 #include "maxsim_common.h"
+#include "maxsim_sched.h"
 
 namespace maxsim {
 
@@ -95,15 +101,14 @@ score_kernel(const ScoreArgs a)
     constexpr float NEG_INF = -__builtin_huge_valf();
 
     extern __shared__ __attribute__((aligned(16))) uint16_t qs[];  // [lq_pad][LDQ]
-    __shared__ uint32_t s_claim_end[kNumBins];   // claims of bins >= b (descending order)
-    __shared__ uint32_t s_desc_start[kNumBins];  // first desc index of bin b
-    __shared__ uint32_t s_chunks[kNumBins];      // chunks per doc in bin b
-    __shared__ float s_comb[kScoreWaves][kMaxLqPad];
+    __shared__ BinTables tab;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int Lq = a.Lq;
     const int lq_pad = a.lq_pad;
+    const uint32_t W = gridDim.x * kScoreWaves;
+    const uint32_t wid = blockIdx.x * kScoreWaves + wave;
 
     // ---- stage Q (zero-padded) into LDS
     {
@@ -118,33 +123,11 @@ score_kernel(const ScoreArgs a)
             *reinterpret_cast<u32x4 *>(qs + r * LDQ + c * 8) = v;
         }
     }
-
-    // ---- schedule: chunk size from the total tile count and this grid's wave count
-    if (threadIdx.x == 0) {
-        const unsigned long long T = a.hdr->total_tiles;
-        const unsigned long long per = (unsigned long long)gridDim.x * kScoreWaves * kItemsPerWave;
-        unsigned long long ct = (T + per - 1) / per;
-        if (ct < kMinChunkTiles) ct = kMinChunkTiles;
-        uint32_t claims = 0, descs = 0;
-        for (int b = kNumBins - 1; b >= 0; --b) {
-            const uint32_t cnt = a.hdr->bin_count[b];
-            const uint32_t cap = 1u << b;  // most tiles a doc of bin b has
-            // cap > ct implies ct < 2^27: 32-bit division suffices.
-            const uint32_t K = cap > ct ? (cap + (uint32_t)ct - 1u) / (uint32_t)ct : 1u;
-            s_desc_start[b] = descs;
-            s_chunks[b] = K;
-            descs += cnt;
-            claims += cnt * K;
-            s_claim_end[b] = claims;
-        }
-    }
+    if (threadIdx.x == 0) fill_bin_tables(a.hdr, W, tab);
     __syncthreads();
 
-    // Per-lane copies of the bin tables (lane b holds bin b), for a ballot search.
-    const uint32_t my_claim_end = lane < kNumBins ? s_claim_end[lane] : 0u;
-    const uint32_t my_desc_start = lane < kNumBins ? s_desc_start[lane] : 0u;
-    const uint32_t my_chunks = lane < kNumBins ? s_chunks[lane] : 1u;
-    const uint32_t total_claims = wave_uniform(__builtin_amdgcn_readlane(my_claim_end, 0));
+    const LaneBins L = lane_bins(tab, lane);
+    const uint32_t total = tab.total_claims;
 
     // ---- per-lane load geometry
     const uint32_t stride_bytes = (uint32_t)a.stride_bytes;
@@ -169,31 +152,37 @@ score_kernel(const ScoreArgs a)
     };
     if (a.ngroups == 1) load_q(0);
 
-    for (;;) {
-        uint32_t g = 0;
-        if (lane == 0) g = atomicAdd(a.claim, 1u);
-        g = wave_uniform(__builtin_amdgcn_readlane(g, 0));
-        if (g >= total_claims) break;
+    // Round r deals item r W + w to wave w (r even) or to wave W-1-w (r odd).
+    auto claim_of = [&](uint32_t r) -> uint32_t {
+        return r * W + ((r & 1u) ? (W - 1u - wid) : wid);
+    };
+    uint32_t r = 0;
+    uint32_t g = claim_of(0);
+    Item nit{};
+    DocDesc nd{};
+    if (g < total) {
+        nit = locate_claim(L, lane, g);
+        nd = a.desc[nit.di];
+    }
 
-        // Bin of claim g: claims run bin 27 first, ..., bin 0 last; g < claim_end[b]
-        // holds exactly for b <= bin(g).
-        const unsigned long long below = __ballot(lane < kNumBins && g < my_claim_end);
-        const int b = 63 - __builtin_clzll(below);
-        const uint32_t bin_end = __builtin_amdgcn_readlane(my_claim_end, b);
-        const uint32_t K = wave_uniform(__builtin_amdgcn_readlane(my_chunks, b));
-        const uint32_t bin_begin = b + 1 < kNumBins ? __builtin_amdgcn_readlane(my_claim_end, b + 1) : 0u;
-        const uint32_t local = g - wave_uniform(bin_begin);
-        (void)bin_end;
-        const uint32_t j = local / K;
-        const uint32_t c = local - j * K;
-        const uint32_t di = wave_uniform(__builtin_amdgcn_readlane(my_desc_start, b)) + j;
-        const DocDesc dd = a.desc[di];
-        const int doc = (int)wave_uniform((uint32_t)dd.doc);
-        const int64_t off = (int64_t)(int32_t)wave_uniform((uint32_t)dd.offset);
-        const int len = (int)wave_uniform((uint32_t)dd.length);
-        const uint32_t nt = wave_uniform((uint32_t)dd.tiles);
+    while (g < total) {
+        const Item it = nit;
+        const int doc = (int)wave_uniform((uint32_t)nd.doc);
+        const int64_t off = (int64_t)(int32_t)wave_uniform((uint32_t)nd.offset);
+        const int len = (int)wave_uniform((uint32_t)nd.length);
+        const uint32_t nt = wave_uniform((uint32_t)nd.tiles);
+        const uint32_t K = it.K;
+        const uint32_t c = it.c;
+        const uint32_t g_cur = g;
 
-        // Tiles [t_begin, t_end) of the doc's nt tiles; never empty (nt >= K).
+        // Next item's descriptor, in flight while this one is scored.
+        g = claim_of(++r);
+        if (g < total) {
+            nit = locate_claim(L, lane, g);
+            nd = a.desc[nit.di];
+        }
+
+        // Tiles [t_begin, t_end) of the doc's nt tiles; never empty unless nt == 0.
         const uint32_t t_begin = (uint32_t)(((unsigned long long)c * nt) / K);
         const uint32_t t_end = (uint32_t)(((unsigned long long)(c + 1) * nt) / K);
         const int ntiles = (int)(t_end - t_begin);
@@ -209,7 +198,7 @@ score_kernel(const ScoreArgs a)
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) rmax[qt][r] = NEG_INF;
+                for (int i = 0; i < 4; ++i) rmax[qt][i] = NEG_INF;
 
             u32x4 buf[P][NKS];
             auto issue = [&](int slot, int t) {
@@ -240,10 +229,10 @@ score_kernel(const ScoreArgs a)
                     if (left < kTileRows) {
                         const bool ok = row_in_tile < left;
 #pragma unroll
-                        for (int r = 0; r < 4; ++r) acc[r] = ok ? acc[r] : NEG_INF;
+                        for (int i = 0; i < 4; ++i) acc[i] = ok ? acc[i] : NEG_INF;
                     }
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) rmax[qt][r] = fmax_plain(rmax[qt][r], acc[r]);
+                    for (int i = 0; i < 4; ++i) rmax[qt][i] = fmax_plain(rmax[qt][i], acc[i]);
                 }
             };
 
@@ -268,54 +257,26 @@ score_kernel(const ScoreArgs a)
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) rmax[qt][r] = row16_max(rmax[qt][r]);
+                for (int i = 0; i < 4; ++i) rmax[qt][i] = row16_max(rmax[qt][i]);
 
             if (K == 1) {
 #pragma unroll
                 for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int q = (grp * NQT + qt) * kTileRows + kgroup * 4 + r;
-                        lane_sum += q < Lq ? rmax[qt][r] : 0.0f;
+                    for (int i = 0; i < 4; ++i) {
+                        const int q = (grp * NQT + qt) * kTileRows + kgroup * 4 + i;
+                        lane_sum += q < Lq ? rmax[qt][i] : 0.0f;
                     }
             } else if (row_in_tile == 0) {
 #pragma unroll
                 for (int qt = 0; qt < NQT; ++qt) {
                     const int q = (grp * NQT + qt) * kTileRows + kgroup * 4;
                     f32x4 v = {rmax[qt][0], rmax[qt][1], rmax[qt][2], rmax[qt][3]};
-                    *reinterpret_cast<f32x4 *>(a.partials + (size_t)g * lq_pad + q) = v;
+                    *reinterpret_cast<f32x4 *>(a.partials + (size_t)g_cur * lq_pad + q) = v;
                 }
             }
         }
-
-        if (K > 1) {
-            // Publish this chunk's maxima, then count it in; the last chunk combines.
-            __threadfence();
-            uint32_t prev = 0;
-            if (lane == 0) prev = atomicAdd(a.arrive + di, 1u);
-            prev = wave_uniform(__builtin_amdgcn_readlane(prev, 0));
-            if (prev != K - 1) continue;
-            __threadfence();
-            const uint32_t first = g - c;
-            for (int q = lane; q < lq_pad; q += kWave) {
-                float m = NEG_INF;
-                for (uint32_t k = 0; k < K; ++k)
-                    m = fmax_plain(m, __builtin_nontemporal_load(a.partials + (size_t)(first + k) * lq_pad + q));
-                s_comb[wave][q] = m;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            for (int grp = 0; grp < a.ngroups; ++grp)
-#pragma unroll
-                for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) {
-                        const int q = (grp * NQT + qt) * kTileRows + kgroup * 4 + r;
-                        lane_sum += q < Lq ? s_comb[wave][q] : 0.0f;
-                    }
-            __builtin_amdgcn_wave_barrier();
-        }
+        if (K > 1) continue;  // the combine kernel finishes split docs
 
         // Fixed-order sum over the four lane groups.
         const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 0));
