@@ -1,8 +1,10 @@
 """Benchmark: MaxSim rerank throughput on one MI355X.
 
 One step = the whole hot path over one batch: the length-binned schedule (two plan
-kernels) and the score kernel, for one query against every doc of the workload, inputs
-already resident in HBM. Prints ONE JSON line.
+kernels), the score kernel and the combine kernel (scores of split docs), for one query
+against every doc of the workload, inputs already resident in HBM. HIP events on the
+launching stream bracket the score kernel alone for the roofline figures. Prints ONE
+JSON line.
 
 Default workload: "large" -- Lq 32, d 128, 80,000 fp16 docs of U[64,448] rows packed
 back to back (~20.5 M doc rows, 5.24 GB; row offset * d passes 2^31), 1 % of docs
@@ -148,6 +150,7 @@ def main() -> int:
         lir.maxsim_score(Q, X, offs, lens, ws, scores=scores)
         if ev_b is not None:
             ev_b.record()
+        lir.maxsim_finish(Q, w.B, ws, scores)
 
     for _ in range(args.warmup):
         step()

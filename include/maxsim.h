@@ -93,19 +93,25 @@ MAXSIM_API const char *maxsim_status_string(int status);
 
 /*
  * Staged form of the same operation, with a caller-owned workspace, for callers that
- * manage scratch memory themselves or time the two stages apart.
+ * manage scratch memory themselves or time the stages apart. The three stages must run
+ * in order on one stream, with the same Lq, d, B and dtype; maxsim_rerank is exactly
+ * plan + score + finish.
  *
- * maxsim_workspace_size: bytes of device workspace that maxsim_plan/maxsim_score need
- *   for these sizes on the current device (depends on the device's compute-unit
- *   count). Writes *bytes. Queries the current device: MAXSIM_ERR_HIP without one.
+ * maxsim_workspace_size: bytes of device workspace the stages need for these sizes
+ *   on the current device (depends on the device's compute-unit count). Writes
+ *   *bytes. Queries the current device: MAXSIM_ERR_HIP without one.
  *
- * maxsim_plan: the length-binned doc schedule. Reads doc_offsets and doc_lengths
- *   and writes the schedule into `workspace` (two kernel launches on `stream`).
- *   The workspace must be 256-byte aligned and at least maxsim_workspace_size bytes.
+ * maxsim_plan: the length-binned doc schedule. Reads doc_offsets and doc_lengths and
+ *   writes the schedule into `workspace` (two kernel launches). The workspace must be
+ *   256-byte aligned and at least maxsim_workspace_size bytes.
  *
- * maxsim_score: the scores. Reads the schedule that maxsim_plan wrote into the same
- *   workspace earlier on the same stream, with the same Lq, d and B, and writes
- *   scores (one kernel launch). dtype is MAXSIM_F16 or MAXSIM_BF16.
+ * maxsim_score: the score kernel (one launch). Writes the score of every doc the
+ *   schedule kept whole; for docs it split into several work items (long docs, when
+ *   the batch is small for the GPU) it writes per-row partial maxima into the
+ *   workspace instead. dtype is MAXSIM_F16 or MAXSIM_BF16.
+ *
+ * maxsim_finish: combines those partial maxima and writes the remaining scores (one
+ *   launch; returns at once on the GPU when no doc was split).
  *
  * A workspace must not be shared by work that may run concurrently.
  */
@@ -119,6 +125,9 @@ MAXSIM_API int maxsim_score(int dtype, const void *Q, int32_t Lq, int32_t d,
                  const void *docs, int64_t stride,
                  const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
                  float *scores, void *workspace, size_t workspace_bytes, void *stream);
+
+MAXSIM_API int maxsim_finish(int dtype, int32_t Lq, int32_t d, int32_t B, float *scores,
+                  void *workspace, size_t workspace_bytes, void *stream);
 
 /* Library version as major*10000 + minor*100 + patch. */
 MAXSIM_API int maxsim_version(void);

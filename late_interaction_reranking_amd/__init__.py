@@ -19,6 +19,7 @@ from .maxsim import (  # noqa: F401
     maxsim_plan,
     maxsim_rerank,
     maxsim_rerank_bf16,
+    maxsim_finish,
     maxsim_score,
     maxsim_status_string,
     maxsim_version,

@@ -93,7 +93,13 @@ struct ScoreArgs {
     float *partials;          // [partial_slots, lq_pad]
     float *scores;
     int32_t Lq, d, ngroups, lq_pad;
+    int32_t q_in_lds;         // Q staged in LDS (else fragments come from global)
 };
+
+// Q is staged in LDS when its padded tile takes at most this many bytes; a larger
+// query (up to 256 x 256) would leave no room for the per-wave doc tiles, so its
+// fragments are read from global memory (L2-resident) instead.
+constexpr size_t kMaxQLdsBytes = 64 * 1024;
 
 // ---------------------------------------------------------------- combine kernel
 struct CombineArgs {

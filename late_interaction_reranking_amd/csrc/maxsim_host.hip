@@ -177,47 +177,67 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
 
 // Split docs: max over each doc's chunk slots, then the score kernel's fixed-order sum
 // (lane l adds, per query tile, rows 4 (l / 16) + 0..3; then lanes 0, 16, 32, 48), so a
-// split doc's score is bitwise the one it would get unsplit. One wave per doc.
+// split doc's score is bitwise the one it would get unsplit. One workgroup per split
+// doc: wave w scans slots w, w + 4, ... with 8 independent loads in flight per lane,
+// the four waves' maxima meet in LDS, and wave 0 sums.
 __global__ void __launch_bounds__(kScoreBlock)
 combine_kernel(const CombineArgs a)
 {
     constexpr float NEG_INF = -__builtin_huge_valf();
+    constexpr int U = 8;
     __shared__ BinTables tab;
-    __shared__ float s_comb[kScoreWaves][kMaxLqPad];
+    __shared__ float s_part[kScoreWaves][kMaxLqPad];
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
-    if (threadIdx.x == 0) fill_bin_tables(a.hdr, a.score_waves, tab);
+    if (wave == 0) fill_bin_tables(a.hdr, a.score_waves, tab, lane);
     __syncthreads();
     const LaneBins L = lane_bins(tab, lane);
     const uint32_t split = tab.split_docs;
     const int kgroup = lane >> 4;
-    float *mx = s_comb[wave];
-    for (uint32_t di = blockIdx.x * kScoreWaves + wave; di < split; di += gridDim.x * kScoreWaves) {
+    const int lq_pad = a.lq_pad;
+    for (uint32_t di = blockIdx.x; di < split; di += gridDim.x) {
         const Item it = locate_doc(L, lane, di);
-        for (int q = lane; q < a.lq_pad; q += kWave) {
+        const float *base = a.partials + (size_t)it.first * lq_pad;
+        for (int q = lane; q < lq_pad; q += kWave) {
             float m = NEG_INF;
-            for (uint32_t k = 0; k < it.K; ++k) {
-                const float v = a.partials[(size_t)(it.first + k) * a.lq_pad + q];
+            uint32_t k = wave;
+            for (; k + (U - 1) * kScoreWaves < it.K; k += U * kScoreWaves) {
+                float v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) v[u] = base[(size_t)(k + u * kScoreWaves) * lq_pad + q];
+#pragma unroll
+                for (int u = 0; u < U; ++u) m = v[u] > m ? v[u] : m;
+            }
+            for (; k < it.K; k += kScoreWaves) {
+                const float v = base[(size_t)k * lq_pad + q];
                 m = v > m ? v : m;
             }
-            mx[q] = m;
+            s_part[wave][q] = m;
         }
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float lane_sum = 0.0f;
-        for (int grp = 0; grp < a.ngroups; ++grp)
-            for (int qt = 0; qt < a.nqt; ++qt)
-                for (int i = 0; i < 4; ++i) {
-                    const int q = (grp * a.nqt + qt) * kTileRows + kgroup * 4 + i;
-                    lane_sum += q < a.Lq ? mx[q] : 0.0f;
-                }
-        __builtin_amdgcn_wave_barrier();
-        const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 0));
-        const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 16));
-        const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 32));
-        const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 48));
-        if (lane == 0) a.scores[a.desc[di].doc] = ((s0 + s1) + s2) + s3;
+        __syncthreads();
+        if (wave == 0) {
+            for (int q = lane; q < lq_pad; q += kWave) {
+                float m = s_part[0][q];
+                for (int w = 1; w < kScoreWaves; ++w) m = s_part[w][q] > m ? s_part[w][q] : m;
+                s_part[0][q] = m;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            float lane_sum = 0.0f;
+            for (int grp = 0; grp < a.ngroups; ++grp)
+                for (int qt = 0; qt < a.nqt; ++qt)
+                    for (int i = 0; i < 4; ++i) {
+                        const int q = (grp * a.nqt + qt) * kTileRows + kgroup * 4 + i;
+                        lane_sum += q < a.Lq ? s_part[0][q] : 0.0f;
+                    }
+            const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 0));
+            const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 16));
+            const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 32));
+            const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 48));
+            if (lane == 0) a.scores[a.desc[di].doc] = ((s0 + s1) + s2) + s3;
+        }
+        __syncthreads();
     }
 }
 
@@ -320,6 +340,17 @@ Config choose_config(int32_t Lq, int32_t d)
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+size_t q_lds_bytes(const Config &c) { return (size_t)c.lq_pad * (c.nks * kStepK + 8) * 2; }
+
+// Dynamic LDS of the score kernel: the Q tile (if it fits the budget), then one staging
+// tile per wave, 16 rows of (d/8 | 1) 16-byte chunks, plus one slot that lanes with
+// nothing to stage write.
+size_t score_lds_bytes(const Config &c, int32_t d)
+{
+    const size_t q = q_lds_bytes(c);
+    return (q <= kMaxQLdsBytes ? q : 0) + (size_t)kScoreWaves * (kTileRows * ((d / 8) | 1) + 1) * 16;
+}
+
 int check_common(const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
                  const int32_t *offsets, const int32_t *lengths, int32_t B, const float *scores)
 {
@@ -374,7 +405,8 @@ int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     const void *fn = dtype == MAXSIM_BF16 ? maxsim_score_kernel_bf16(c.nks, c.nqt)
                                           : maxsim_score_kernel_f16(c.nks, c.nqt);
     if (!fn) return MAXSIM_ERR_UNSUPPORTED;
-    const size_t lds = (size_t)c.lq_pad * (c.nks * kStepK + 8) * 2;
+    const bool q_in_lds = q_lds_bytes(c) <= kMaxQLdsBytes;
+    const size_t lds = score_lds_bytes(c, d);
     int per_cu = 0;
     if (score_blocks_per_cu(fn, lds, &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     DeviceFacts f;
@@ -391,22 +423,38 @@ int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     a.d = d;
     a.ngroups = c.ngroups;
     a.lq_pad = c.lq_pad;
+    a.q_in_lds = q_in_lds ? 1 : 0;
     void *args[] = {&a};
     const dim3 grid((unsigned)(f.cus * per_cu));
     if (hipLaunchKernel(fn, grid, dim3(kScoreBlock), args, lds, stream) != hipSuccess) return MAXSIM_ERR_HIP;
-    if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
+}
 
+// The combine kernel recomputes the score kernel's chunking, which depends on that
+// launch's wave count: the same instance and occupancy are looked up here.
+int launch_finish(int dtype, int32_t Lq, int32_t d, float *scores, const Layout &L, char *ws,
+                  hipStream_t stream)
+{
+    const Config c = choose_config(Lq, d);
+    if (c.lq_pad > kMaxLqPad || c.nqt * c.nks > kMaxFragsPerGroup) return MAXSIM_ERR_UNSUPPORTED;
+    const void *fn = dtype == MAXSIM_BF16 ? maxsim_score_kernel_bf16(c.nks, c.nqt)
+                                          : maxsim_score_kernel_f16(c.nks, c.nqt);
+    if (!fn) return MAXSIM_ERR_UNSUPPORTED;
+    int per_cu = 0;
+    if (score_blocks_per_cu(fn, score_lds_bytes(c, d), &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    DeviceFacts f;
+    if (current_facts(&f) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     CombineArgs ca;
-    ca.hdr = a.hdr;
-    ca.desc = a.desc;
-    ca.partials = a.partials;
+    ca.hdr = reinterpret_cast<const Header *>(ws + L.header);
+    ca.desc = reinterpret_cast<const DocDesc *>(ws + L.desc);
+    ca.partials = reinterpret_cast<const float *>(ws + L.partials);
     ca.scores = scores;
-    ca.score_waves = grid.x * kScoreWaves;
+    ca.score_waves = (uint32_t)(f.cus * per_cu * kScoreWaves);
     ca.Lq = Lq;
     ca.nqt = c.nqt;
     ca.ngroups = c.ngroups;
     ca.lq_pad = c.lq_pad;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)f.cus), dim3(kScoreBlock), 0, stream, ca);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)f.cus * 4u), dim3(kScoreBlock), 0, stream, ca);
     return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
 }
 
@@ -425,6 +473,7 @@ int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, in
     int rc = launch_plan(offsets, lengths, B, L, static_cast<char *>(ws), stream);
     if (rc == MAXSIM_OK)
         rc = launch_score(dtype, Q, Lq, d, docs, stride, B, scores, L, static_cast<char *>(ws), stream);
+    if (rc == MAXSIM_OK) rc = launch_finish(dtype, Lq, d, scores, L, static_cast<char *>(ws), stream);
     if (hipFreeAsync(ws, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
     return rc;
 }
@@ -499,6 +548,23 @@ int maxsim_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
     return launch_score(dtype, Q, Lq, d, docs, stride, B, scores, L, static_cast<char *>(workspace), s);
+}
+
+int maxsim_finish(int dtype, int32_t Lq, int32_t d, int32_t B, float *scores, void *workspace,
+                  size_t workspace_bytes, void *stream)
+{
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
+    if (B < 0 || Lq < 0 || d < 1) return MAXSIM_ERR_INVALID_ARG;
+    if (B > 0 && !scores) return MAXSIM_ERR_INVALID_ARG;
+    if (d > kMaxD || d % 8 != 0 || Lq > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
+    if (B > 0 && ((uintptr_t)scores & 3u)) return MAXSIM_ERR_INVALID_ARG;
+    if (B == 0 || Lq == 0) return MAXSIM_OK;
+    if (!workspace || ((uintptr_t)workspace & 255u)) return MAXSIM_ERR_WORKSPACE;
+    Layout L;
+    if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
+    return launch_finish(dtype, Lq, d, scores, L, static_cast<char *>(workspace),
+                         static_cast<hipStream_t>(stream));
 }
 
 int maxsim_version(void) { return 100; }

@@ -23,8 +23,9 @@ struct BinTables {
     uint32_t split_docs;            // docs with K_b > 1: desc indices [0, split_docs)
 };
 
-// One thread fills the tables; the caller publishes them with a barrier.
-__device__ inline void fill_bin_tables(const Header *hdr, uint32_t waves, BinTables &t)
+// Wave 0 of a workgroup fills the tables (lane b computes bin b, lane 0 scans the
+// bins in descending order); the caller publishes them with a barrier.
+__device__ inline void fill_bin_tables(const Header *hdr, uint32_t waves, BinTables &t, int lane)
 {
     const unsigned long long T = hdr->total_tiles;
     const unsigned long long per = (unsigned long long)waves * kItemsPerWave;
@@ -32,20 +33,30 @@ __device__ inline void fill_bin_tables(const Header *hdr, uint32_t waves, BinTab
     if (ct < kMinChunkTiles) ct = kMinChunkTiles;
     if (ct > (1ull << 28)) ct = 1ull << 28;  // above every bin's 2^b: no splits
     const uint32_t ct32 = (uint32_t)ct;
-    uint32_t claims = 0, descs = 0, split = 0;
-    for (int b = kNumBins - 1; b >= 0; --b) {
-        const uint32_t cnt = hdr->bin_count[b];
-        const uint32_t cap = 1u << b;  // most tiles a doc of bin b has
+    if (lane < kNumBins) {
+        const uint32_t cnt = hdr->bin_count[lane];
+        const uint32_t cap = 1u << lane;  // most tiles a doc of bin `lane` has
         const uint32_t K = cap > ct32 ? (cap + ct32 - 1u) / ct32 : 1u;
-        t.desc_start[b] = descs;
-        t.chunks[b] = K;
-        if (K > 1) split += cnt;
-        descs += cnt;
-        claims += cnt * K;
-        t.claim_end[b] = claims;
+        t.chunks[lane] = K;
+        t.desc_start[lane] = cnt;       // counts for now, turned into starts below
+        t.claim_end[lane] = cnt * K;    // claims of the bin for now
     }
-    t.total_claims = claims;
-    t.split_docs = split;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane == 0) {
+        uint32_t claims = 0, descs = 0, split = 0;
+        for (int b = kNumBins - 1; b >= 0; --b) {
+            const uint32_t cnt = t.desc_start[b];
+            if (t.chunks[b] > 1) split += cnt;
+            t.desc_start[b] = descs;
+            descs += cnt;
+            claims += t.claim_end[b];
+            t.claim_end[b] = claims;
+        }
+        t.total_claims = claims;
+        t.split_docs = split;
+    }
 }
 
 // Per-lane copy of the tables (lane b < kNumBins holds bin b) for ballot searches.

@@ -13,25 +13,36 @@
 //     alternating direction (round r gives item r W + w to wave w, or to wave W-1-w
 //     when r is odd), so every wave gets a similar mix of long and short items. No
 //     atomics: a shared claim counter serialises across the chip's eight XCDs.
-//     Each wave loads the descriptor of its next item while it scores the current one.
+//   - Each wave runs its items as one continuous stream of tiles: the last pipeline
+//     slots of one item already load the next item's first tiles, and descriptors are
+//     fetched two items ahead, so the load pipeline never drains between items.
 //   - Q is staged once per workgroup into LDS, zero-padded to 16-row tiles and
-//     32-column K-steps. Each wave keeps its MFMA A-fragments of one group of up to
-//     NQT query tiles in registers; with one group (every Lq * d that fits 128 VGPRs)
-//     they are loaded once for the kernel's lifetime.
-//   - Doc rows are read in 16-row tiles. Lane l owns row (l % 16) of the tile and, in
-//     K-step s, the 8 contiguous elements starting at column 8 * (4 s + l / 16): one
-//     128-bit buffer load per lane per K-step, i.e. exactly the B-fragment layout of
-//     v_mfma_f32_16x16x32_{f16,bf16}. A and B use the same lane -> column mapping, so
-//     the dot products are exact dot products whatever the order inside a fragment.
+//     32-column K-steps (when the padded tile fits 64 KB; a larger query's fragments
+//     are read from global memory). Each wave keeps its MFMA A-fragments of one group
+//     of up to NQT query tiles in registers; with one group (every Lq * d that fits
+//     128 VGPRs) they are loaded once for the kernel's lifetime.
+//   - Doc rows are read in 16-row tiles with coalesced, non-temporal 128-bit buffer
+//     loads: load s, lane l takes 16-byte chunk e = 64 s + l of the tile (row e / C,
+//     chunk e % C, C = d / 8), so one load instruction reads 1 KB of consecutive row
+//     bytes. (The
+//     MFMA operand layout read straight from memory touches 16 rows x 64 B per
+//     instruction, half of 16 cache lines, and streams ~13 % slower on this chip.)
+//     Each wave then writes the tile into its own LDS buffer, rows C | 1 chunks apart
+//     (odd pitch: conflict-free reads), and reads it back in the B-fragment layout of
+//     v_mfma_f32_16x16x32_{f16,bf16}: lane l, K-step s gets row (l % 16), columns
+//     8 (4 s + l / 16) .. +7. A and B use the same lane -> column mapping, so the dot
+//     products are exact dot products whatever the order inside a fragment.
 //   - The row address is a 64-bit scalar base (doc offset widened to int64 before it
 //     is multiplied by the stride, as the page's kernel does) plus a 32-bit per-lane
 //     offset. Each tile gets a buffer descriptor whose size covers only the tile's
 //     valid rows, so rows past the end of the doc read as zero and are never fetched;
-//     K-chunks past d are pushed out of range the same way.
+//     chunks past the tile (when 16 C is not a multiple of 64) are pushed out of
+//     range the same way, and K-columns past d are zeroed in the fragment.
 //   - S = Qtile . Dtile^T lands with lane l holding doc row (l % 16) and query rows
-//     4 (l / 16) + j, j < 4. Invalid doc rows are set to -inf (only on a partial
-//     tile), then an element-wise running max per lane; at the end of the item four
-//     DPP row_ror steps (8, 4, 2, 1) take the max over the 16 doc-row lanes.
+//     4 (l / 16) + j, j < 4. The accumulator of an invalid doc row (past the doc's
+//     end) starts at -inf instead of 0, which keeps it at -inf; then an element-wise
+//     running max per lane; at the end of the item four DPP row_ror steps
+//     (8, 4, 2, 1) take the max over the 16 doc-row lanes.
 //   - Query rows past Lq (zero padding) are masked to 0 and the per-row maxima are
 //     summed in one fixed order (ascending query tile, then j, then the four lane
 //     groups), whether the doc was scored in one item or several, so scores do not
@@ -55,6 +66,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // Buffer descriptor word 3 for raw (unswizzled, unformatted) access on gfx9-family.
 constexpr int kBufferWord3 = 0x00020000;
+// Cache policy of the doc-row loads: non-temporal (streaming). Every doc byte is read
+// exactly once; with the default policy the same stream runs ~12 % slower on MI355X
+// (6.2 vs 6.9 TB/s measured for plain 1 KB-per-instruction reads).
+constexpr int kDocLoadPolicy = 2;
 
 template <bool BF16>
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c)
@@ -92,26 +107,33 @@ __device__ __forceinline__ uint32_t wave_uniform(uint32_t v)
     return __builtin_amdgcn_readfirstlane(v);
 }
 
-template <int NKS, int NQT, bool BF16, int P>
-__global__ void __launch_bounds__(kScoreBlock)
+__device__ __forceinline__ uint64_t wave_uniform64(uint64_t v)
+{
+    return (uint64_t)wave_uniform((uint32_t)v) | ((uint64_t)wave_uniform((uint32_t)(v >> 32)) << 32);
+}
+
+// MINW: waves per SIMD the register allocation must allow (512 / MINW registers).
+template <int NKS, int NQT, bool BF16, int P, int MINW>
+__global__ void __launch_bounds__(kScoreBlock, MINW)
 score_kernel(const ScoreArgs a)
 {
     constexpr int DPAD = NKS * kStepK;
     constexpr int LDQ = DPAD + 8;  // LDS row pitch (halves): 16 B skew against bank conflicts
     constexpr float NEG_INF = -__builtin_huge_valf();
 
-    extern __shared__ __attribute__((aligned(16))) uint16_t qs[];  // [lq_pad][LDQ]
+    extern __shared__ __attribute__((aligned(16))) uint16_t qs[];  // [lq_pad][LDQ], then per-wave tiles
     __shared__ BinTables tab;
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const int Lq = a.Lq;
     const int lq_pad = a.lq_pad;
+    const int ngroups = a.ngroups;
     const uint32_t W = gridDim.x * kScoreWaves;
     const uint32_t wid = blockIdx.x * kScoreWaves + wave;
 
     // ---- stage Q (zero-padded) into LDS
-    {
+    if (a.q_in_lds) {
         constexpr int CPR = DPAD / 8;  // 16-byte chunks per padded row
         const int n = lq_pad * CPR;
         for (int e = threadIdx.x; e < n; e += kScoreBlock) {
@@ -123,21 +145,35 @@ score_kernel(const ScoreArgs a)
             *reinterpret_cast<u32x4 *>(qs + r * LDQ + c * 8) = v;
         }
     }
-    if (threadIdx.x == 0) fill_bin_tables(a.hdr, W, tab);
+    if (wave == 0) fill_bin_tables(a.hdr, W, tab, lane);
     __syncthreads();
 
     const LaneBins L = lane_bins(tab, lane);
     const uint32_t total = tab.total_claims;
 
-    // ---- per-lane load geometry
+    // ---- per-lane load and staging geometry
     const uint32_t stride_bytes = (uint32_t)a.stride_bytes;
     const int row_in_tile = lane & 15;
     const int kgroup = lane >> 4;
-    const uint32_t voff = (uint32_t)row_in_tile * stride_bytes + (uint32_t)kgroup * 16u;
-    // K-step NKS-1 may hold 8-column chunks past d; those lanes point at row 16 of the
-    // tile, which no tile descriptor covers (it spans at most 16 rows), so they read 0.
-    const bool last_chunk_ok = ((NKS - 1) * 4 + kgroup) * 8 < a.d;
-    const uint32_t voff_last = last_chunk_ok ? voff + (NKS - 1) * 64u : (uint32_t)kTileRows * stride_bytes;
+    const int C = a.d / 8;           // 16-byte chunks per row
+    const int pitch = C | 1;         // LDS row pitch in chunks
+    const int dummy = kTileRows * pitch;  // LDS slot for lanes with nothing to stage
+    u32x4 *tile = reinterpret_cast<u32x4 *>(qs + (a.q_in_lds ? lq_pad * LDQ : 0)) + wave * (dummy + 1);
+    uint32_t ld_off[NKS];            // byte offset in the tile of load s
+    int st_idx[NKS];                 // LDS chunk index it is staged to
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        const int e = s * kWave + lane;
+        const int row = e / C;
+        const int ch = e - row * C;
+        const bool ok = e < kTileRows * C;
+        // Chunks past the tile point at row 16, which no tile descriptor covers.
+        ld_off[s] = ok ? (uint32_t)row * stride_bytes + (uint32_t)ch * 16u : (uint32_t)kTileRows * stride_bytes;
+        st_idx[s] = ok ? row * pitch + ch : dummy;
+    }
+    const int rd_idx = row_in_tile * pitch + kgroup;  // + 4 s for K-step s
+    // K-step NKS-1 may hold 8-column chunks past d: those fragment lanes are zero.
+    const bool last_chunk_ok = (NKS - 1) * 4 + kgroup < C;
 
     u32x4 qf[NQT][NKS];
     auto load_q = [&](int grp) {
@@ -147,143 +183,208 @@ score_kernel(const ScoreArgs a)
             for (int s = 0; s < NKS; ++s) {
                 const int row = (grp * NQT + qt) * kTileRows + row_in_tile;
                 const int col = (s * 4 + kgroup) * 8;
-                qf[qt][s] = *reinterpret_cast<const u32x4 *>(qs + row * LDQ + col);
+                if (a.q_in_lds) {
+                    qf[qt][s] = *reinterpret_cast<const u32x4 *>(qs + row * LDQ + col);
+                } else {
+                    u32x4 v = {0u, 0u, 0u, 0u};
+                    if (row < Lq && col < a.d)
+                        v = *reinterpret_cast<const u32x4 *>(a.Q + (size_t)row * a.d + col);
+                    qf[qt][s] = v;
+                }
             }
     };
-    if (a.ngroups == 1) load_q(0);
+    if (ngroups == 1) load_q(0);
 
-    // Round r deals item r W + w to wave w (r even) or to wave W-1-w (r odd).
+    // ---- the wave's items: round r deals item r W + w to wave w (r even) or to wave
+    // W-1-w (r odd)
     auto claim_of = [&](uint32_t r) -> uint32_t {
         return r * W + ((r & 1u) ? (W - 1u - wid) : wid);
     };
+    struct Span {  // one work item, resolved to rows; every field wave-uniform
+        uint64_t base;   // address of its first row
+        int nrows;
+        int ntiles;
+        int doc;
+        uint32_t K;      // chunks of its doc (1: the item is the whole doc)
+        uint32_t g;      // claim index (slot of its partial maxima when K > 1)
+        bool valid;
+    };
+    auto fetch = [&](uint32_t g, Item &it, DocDesc &dd) {
+        if (g < total) {
+            it = locate_claim(L, lane, g);
+            dd = a.desc[it.di];
+        }
+    };
+    auto resolve = [&](uint32_t g, const Item &it, const DocDesc &dd) -> Span {
+        Span sp;
+        sp.valid = g < total;
+        sp.g = g;
+        if (!sp.valid) {
+            sp.base = (uint64_t)(uintptr_t)a.docs;
+            sp.nrows = sp.ntiles = sp.doc = 0;
+            sp.K = 1;
+            return sp;
+        }
+        sp.doc = (int)wave_uniform((uint32_t)dd.doc);
+        const int64_t off = (int64_t)(int32_t)wave_uniform((uint32_t)dd.offset);
+        const int len = (int)wave_uniform((uint32_t)dd.length);
+        const uint32_t nt = wave_uniform((uint32_t)dd.tiles);
+        sp.K = it.K;
+        // Tiles [t_begin, t_end) of the doc's nt tiles; never empty unless nt == 0.
+        const uint32_t t_begin = (uint32_t)(((unsigned long long)it.c * nt) / it.K);
+        const uint32_t t_end = (uint32_t)(((unsigned long long)(it.c + 1) * nt) / it.K);
+        sp.ntiles = (int)(t_end - t_begin);
+        const int row0 = (int)t_begin * kTileRows;
+        sp.nrows = (len < (int)t_end * kTileRows ? len : (int)t_end * kTileRows) - row0;
+        sp.base = (uint64_t)(uintptr_t)a.docs + (uint64_t)((off + row0) * a.stride_bytes);
+        return sp;
+    };
+
+    u32x4 buf[P][NKS];
+    // Loads of tile t of span sp into pipeline slot `slot`. The descriptor covers only
+    // the tile's valid rows (none for t past the span, or for an invalid span).
+    auto issue = [&](int slot, uint64_t base, int nrows, int t) {
+        const int left = nrows - t * kTileRows;
+        const uint32_t rows = left <= 0 ? 0u : (left >= kTileRows ? (uint32_t)kTileRows : (uint32_t)left);
+        const uint64_t ub = wave_uniform64(base + (uint64_t)t * kTileRows * stride_bytes);
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void *>((uintptr_t)ub), (short)0, (int)wave_uniform(rows * stride_bytes), kBufferWord3);
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+            buf[slot][s] = __builtin_bit_cast(
+                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)ld_off[s], 0, kDocLoadPolicy));
+    };
+
+    float rmax[NQT][4];
+    // Tile t (in slot `slot`) of a span with `nrows` rows: stage, multiply, max.
+    auto consume = [&](int slot, int nrows, int t) {
+        const int left = nrows - t * kTileRows;
+        // Coalesced layout -> MFMA B-fragment layout through this wave's LDS buffer
+        // (the LDS operations of one wave complete in order).
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) tile[st_idx[s]] = buf[slot][s];
+        u32x4 bf[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            bf[s] = tile[rd_idx + 4 * s];
+            if (s == NKS - 1 && !last_chunk_ok) bf[s] = u32x4{0u, 0u, 0u, 0u};
+        }
+        // The accumulator starts at 0 for this lane's doc row if the row is valid and
+        // at -inf if not (past the doc end): -inf + a finite dot stays -inf, so invalid
+        // rows never win the max and need no masking.
+        const float c0 = row_in_tile < left ? 0.0f : NEG_INF;
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            f32x4 acc = {c0, c0, c0, c0};
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) acc = mfma16x16x32<BF16>(qf[qt][s], bf[s], acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rmax[qt][i] = __builtin_fmaxf(rmax[qt][i], acc[i]);
+        }
+    };
+
+    // Descriptor queue: cur and nxt resolved, the one after that in flight.
     uint32_t r = 0;
-    uint32_t g = claim_of(0);
-    Item nit{};
-    DocDesc nd{};
-    if (g < total) {
-        nit = locate_claim(L, lane, g);
-        nd = a.desc[nit.di];
+    Item i0{}, i1{}, i2{};
+    DocDesc d0{}, d1{}, d2{};
+    const uint32_t g0 = claim_of(r++);
+    const uint32_t g1 = claim_of(r++);
+    fetch(g0, i0, d0);
+    fetch(g1, i1, d1);
+    Span cur = resolve(g0, i0, d0);
+    Span nxt = resolve(g1, i1, d1);
+    uint32_t g2 = g1;
+
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        issue(p, cur.base, cur.nrows, p);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
-    while (g < total) {
-        const Item it = nit;
-        const int doc = (int)wave_uniform((uint32_t)nd.doc);
-        const int64_t off = (int64_t)(int32_t)wave_uniform((uint32_t)nd.offset);
-        const int len = (int)wave_uniform((uint32_t)nd.length);
-        const uint32_t nt = wave_uniform((uint32_t)nd.tiles);
-        const uint32_t K = it.K;
-        const uint32_t c = it.c;
-        const uint32_t g_cur = g;
-
-        // Next item's descriptor, in flight while this one is scored.
-        g = claim_of(++r);
-        if (g < total) {
-            nit = locate_claim(L, lane, g);
-            nd = a.desc[nit.di];
+    // Sub-items: (item, query group). The tiles of a sub-item run as one pipelined
+    // stream that ends by loading the first tiles of the next sub-item (the same item's
+    // next query group, or the next item).
+    int grp = 0;
+    float lane_sum = 0.0f;
+    while (wave_uniform(cur.valid ? 1u : 0u)) {
+        if (grp == 0) {
+            g2 = claim_of(r++);
+            fetch(g2, i2, d2);
         }
+        if (ngroups > 1) load_q(grp);
+        // Everything that steers the tile loop is wave-uniform; restate it so that it
+        // stays in scalar registers (the loads' descriptors are built from it).
+        const bool more_groups = grp + 1 < ngroups;
+        const uint64_t c_base = wave_uniform64(cur.base);
+        const int c_rows = (int)wave_uniform((uint32_t)cur.nrows);
+        // An empty doc runs as one tile with no valid rows (zero-size loads, all
+        // accumulators -inf): its maxima stay -inf, and the loop shape never changes.
+        const int c_tiles = (int)wave_uniform((uint32_t)(cur.ntiles > 0 ? cur.ntiles : 1));
+        const uint64_t n_base = wave_uniform64(more_groups ? cur.base : nxt.base);
+        const int n_rows = (int)wave_uniform((uint32_t)(more_groups ? cur.nrows : nxt.nrows));
 
-        // Tiles [t_begin, t_end) of the doc's nt tiles; never empty unless nt == 0.
-        const uint32_t t_begin = (uint32_t)(((unsigned long long)c * nt) / K);
-        const uint32_t t_end = (uint32_t)(((unsigned long long)(c + 1) * nt) / K);
-        const int ntiles = (int)(t_end - t_begin);
-        const int row0 = (int)t_begin * kTileRows;
-        const int nrows = (len < (int)t_end * kTileRows ? len : (int)t_end * kTileRows) - row0;
-        const char *chunk_base = a.docs + (off + row0) * a.stride_bytes;
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rmax[qt][i] = NEG_INF;
 
-        float lane_sum = 0.0f;
-        for (int grp = 0; grp < a.ngroups; ++grp) {
-            if (a.ngroups > 1) load_q(grp);
-
-            float rmax[NQT][4];
-#pragma unroll
-            for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) rmax[qt][i] = NEG_INF;
-
-            u32x4 buf[P][NKS];
-            auto issue = [&](int slot, int t) {
-                const int left = nrows - t * kTileRows;
-                const uint32_t rows = left <= 0 ? 0u : (left >= kTileRows ? (uint32_t)kTileRows : (uint32_t)left);
-                // Every field of the descriptor is wave-uniform; say so, so that it
-                // lives in scalar registers.
-                const uint64_t base = (uint64_t)(uintptr_t)chunk_base + (uint64_t)t * kTileRows * stride_bytes;
-                const uint64_t ubase = (uint64_t)wave_uniform((uint32_t)base) |
-                                       ((uint64_t)wave_uniform((uint32_t)(base >> 32)) << 32);
-                const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-                    reinterpret_cast<void *>((uintptr_t)ubase), (short)0,
-                    (int)wave_uniform(rows * stride_bytes), kBufferWord3);
-#pragma unroll
-                for (int s = 0; s < NKS; ++s) {
-                    const uint32_t vo = s == NKS - 1 ? voff_last : voff + s * 64u;
-                    buf[slot][s] = __builtin_bit_cast(
-                        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)vo, 0, 0));
-                }
-            };
-            auto consume = [&](int slot, int t) {
-                const int left = nrows - t * kTileRows;
-#pragma unroll
-                for (int qt = 0; qt < NQT; ++qt) {
-                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                    for (int s = 0; s < NKS; ++s) acc = mfma16x16x32<BF16>(qf[qt][s], buf[slot][s], acc);
-                    if (left < kTileRows) {
-                        const bool ok = row_in_tile < left;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) acc[i] = ok ? acc[i] : NEG_INF;
-                    }
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) rmax[qt][i] = fmax_plain(rmax[qt][i], acc[i]);
-                }
-            };
-
-            // Software pipeline, P tiles deep: the loads of tile t + P are issued as
-            // soon as tile t has been consumed. The scheduling barriers keep the
-            // issue order fixed, so each consume waits only for its own tile's loads.
+        // Software pipeline, P tiles deep, over the span's tiles rounded up to P; the
+        // scheduling barriers keep the issue order fixed, so each tile waits only for
+        // its own loads.
+        const int ntp = (c_tiles + P - 1) / P * P;
+        for (int t0 = 0; t0 < ntp; t0 += P) {
 #pragma unroll
             for (int p = 0; p < P; ++p) {
-                issue(p, p);
+                const int t = t0 + p;
+                if (t < c_tiles) consume(p, c_rows, t);
+                __builtin_amdgcn_sched_barrier(0);
+                // Tile t + P of this sub-item, or, past its end, of the next one.
+                const int ti = t + P;
+                const bool tail = ti >= ntp;
+                issue(p, tail ? n_base : c_base, tail ? n_rows : c_rows, tail ? ti - ntp : ti);
                 __builtin_amdgcn_sched_barrier(0);
             }
-            for (int t0 = 0; t0 < ntiles; t0 += P) {
-#pragma unroll
-                for (int p = 0; p < P; ++p) {
-                    consume(p, t0 + p);
-                    __builtin_amdgcn_sched_barrier(0);
-                    issue(p, t0 + p + P);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
+        }
 
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rmax[qt][i] = row16_max(rmax[qt][i]);
+
+        if (cur.K == 1) {
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) rmax[qt][i] = row16_max(rmax[qt][i]);
-
-            if (K == 1) {
-#pragma unroll
-                for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-                    for (int i = 0; i < 4; ++i) {
-                        const int q = (grp * NQT + qt) * kTileRows + kgroup * 4 + i;
-                        lane_sum += q < Lq ? rmax[qt][i] : 0.0f;
-                    }
-            } else if (row_in_tile == 0) {
-#pragma unroll
-                for (int qt = 0; qt < NQT; ++qt) {
-                    const int q = (grp * NQT + qt) * kTileRows + kgroup * 4;
-                    f32x4 v = {rmax[qt][0], rmax[qt][1], rmax[qt][2], rmax[qt][3]};
-                    *reinterpret_cast<f32x4 *>(a.partials + (size_t)g_cur * lq_pad + q) = v;
+                for (int i = 0; i < 4; ++i) {
+                    const int q = (grp * NQT + qt) * kTileRows + kgroup * 4 + i;
+                    lane_sum += q < Lq ? rmax[qt][i] : 0.0f;
                 }
+        } else if (row_in_tile == 0) {
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                const int q = (grp * NQT + qt) * kTileRows + kgroup * 4;
+                f32x4 v = {rmax[qt][0], rmax[qt][1], rmax[qt][2], rmax[qt][3]};
+                *reinterpret_cast<f32x4 *>(a.partials + (size_t)cur.g * lq_pad + q) = v;
             }
         }
-        if (K > 1) continue;  // the combine kernel finishes split docs
-
-        // Fixed-order sum over the four lane groups.
-        const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 0));
-        const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 16));
-        const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 32));
-        const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 48));
-        if (lane == 0) a.scores[doc] = ((s0 + s1) + s2) + s3;
+        if (more_groups) {
+            ++grp;
+            continue;
+        }
+        if (cur.K == 1) {
+            // Fixed-order sum over the four lane groups.
+            const int ls = __builtin_bit_cast(int, lane_sum);
+            const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 0));
+            const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 16));
+            const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 32));
+            const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
+            if (lane == 0) a.scores[cur.doc] = ((s0 + s1) + s2) + s3;
+        }
+        // (split docs: the combine kernel finishes them)
+        lane_sum = 0.0f;
+        grp = 0;
+        cur = nxt;
+        nxt = resolve(g2, i2, d2);
     }
 }
 

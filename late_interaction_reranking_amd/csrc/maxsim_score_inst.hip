@@ -14,14 +14,32 @@ namespace {
 
 constexpr int NKS = MAXSIM_NKS;
 constexpr bool BF = MAXSIM_BF16 != 0;
-// Pipeline depth in doc tiles: 8-12 KB of loads outstanding per wave.
-constexpr int P = NKS >= 5 ? 2 : (NKS >= 3 ? 3 : (NKS == 2 ? 5 : 8));
+// Pipeline depth in doc tiles: 4-8 KB of coalesced loads outstanding per wave.
+#ifdef MAXSIM_FORCE_P
+constexpr int P = MAXSIM_FORCE_P;
+#else
+constexpr int P = NKS >= 3 ? 2 : (NKS == 2 ? 3 : 4);
+#endif
+
+// Occupancy target (waves per SIMD) from an estimate of the registers one wave needs:
+// query fragments, P tiles of loads in flight, one staged fragment set, running
+// maxima and accumulators, plus addressing and loop state.
+template <int NQT>
+constexpr int min_waves()
+{
+#ifdef MAXSIM_FORCE_MINW
+    return MAXSIM_FORCE_MINW;
+#else
+    constexpr int est = 4 * NQT * NKS + 4 * P * NKS + 4 * NKS + 8 * NQT + 56;
+    return est <= 128 ? 4 : (est <= 168 ? 3 : (est <= 256 ? 2 : 1));
+#endif
+}
 
 template <int NQT>
 const void *entry()
 {
     if constexpr (NQT * NKS <= maxsim::kMaxFragsPerGroup)
-        return reinterpret_cast<const void *>(&maxsim::score_kernel<NKS, NQT, BF, P>);
+        return reinterpret_cast<const void *>(&maxsim::score_kernel<NKS, NQT, BF, P, min_waves<NQT>()>);
     else
         return nullptr;
 }

@@ -9,6 +9,7 @@ The functions carry the C ABI's names (include/maxsim.h) and take torch tensors:
     maxsim_workspace_size(Lq, d, B) -> bytes
     maxsim_plan(doc_offsets, doc_lengths, Lq, d, workspace)
     maxsim_score(Q, docs, doc_offsets, doc_lengths, workspace, scores=None)
+    maxsim_finish(Q, B, workspace, scores)
     rerank(...)  picks maxsim_rerank or maxsim_rerank_bf16 from Q's dtype
 
 Q is [Lq, d] and contiguous; docs is a 2-D view whose rows are docs.stride(0) elements
@@ -36,6 +37,7 @@ __all__ = [
     "maxsim_workspace_size",
     "maxsim_plan",
     "maxsim_score",
+    "maxsim_finish",
     "maxsim_version",
     "rerank",
     "MAXSIM_F16",
@@ -87,6 +89,8 @@ def load() -> ctypes.CDLL:
         lib.maxsim_plan.argtypes = [P, P, I32, I32, I32, P, SZ, P]
         lib.maxsim_score.restype = ctypes.c_int
         lib.maxsim_score.argtypes = [ctypes.c_int, P, I32, I32, P, I64, P, P, I32, P, P, SZ, P]
+        lib.maxsim_finish.restype = ctypes.c_int
+        lib.maxsim_finish.argtypes = [ctypes.c_int, I32, I32, I32, P, P, SZ, P]
         lib.maxsim_version.restype = ctypes.c_int
         lib.maxsim_version.argtypes = []
         _lib = lib
@@ -194,7 +198,8 @@ def maxsim_plan(doc_offsets, doc_lengths, Lq: int, d: int, workspace: torch.Tens
 
 
 def maxsim_score(Q, docs, doc_offsets, doc_lengths, workspace: torch.Tensor, scores=None) -> torch.Tensor:
-    """Enqueue the score kernel over a schedule maxsim_plan wrote into `workspace`."""
+    """Enqueue the score kernel over a schedule maxsim_plan wrote into `workspace`.
+    Docs the schedule split are completed by maxsim_finish."""
     dtype = torch.bfloat16 if Q.dtype == torch.bfloat16 else torch.float16
     Lq, d, stride, B = _marshal(Q, docs, doc_offsets, doc_lengths, dtype)
     if scores is None:
@@ -206,4 +211,20 @@ def maxsim_score(Q, docs, doc_offsets, doc_lengths, workspace: torch.Tensor, sco
                                  doc_offsets.data_ptr(), doc_lengths.data_ptr(), B,
                                  scores.data_ptr(), ptr, nbytes, _stream(docs))
     _check(st, "maxsim_score")
+    return scores
+
+
+def maxsim_finish(Q, B: int, workspace: torch.Tensor, scores: torch.Tensor) -> torch.Tensor:
+    """Enqueue the combine step: the scores of docs the schedule split into several
+    work items. Q only supplies Lq, d and the element format."""
+    if Q.dim() != 2:
+        raise ValueError("Q must be 2-D")
+    if scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    code = MAXSIM_BF16 if Q.dtype == torch.bfloat16 else MAXSIM_F16
+    ptr, nbytes = _ws(workspace)
+    with torch.cuda.device(workspace.device):
+        st = load().maxsim_finish(code, int(Q.shape[0]), int(Q.shape[1]), int(B), scores.data_ptr(),
+                                  ptr, nbytes, _stream(workspace))
+    _check(st, "maxsim_finish")
     return scores

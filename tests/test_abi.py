@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("maxsim_rerank", "maxsim_rerank_bf16", "maxsim_status_string",
-              "maxsim_workspace_size", "maxsim_plan", "maxsim_score", "maxsim_version"):
+              "maxsim_workspace_size", "maxsim_plan", "maxsim_score", "maxsim_finish",
+              "maxsim_version"):
         assert n in names
 
 
@@ -104,6 +105,12 @@ def test_staged_validation(lib):
     assert lib.maxsim_plan(FAKE, FAKE, -2, 32, 128, FAKE, 1 << 20, None) == INVALID
     assert lib.maxsim_plan(FAKE, FAKE, 4, 32, 100, FAKE, 1 << 20, None) == UNSUPPORTED
     assert lib.maxsim_plan(FAKE, FAKE, 0, 32, 128, None, 0, None) == OK
+    assert lib.maxsim_finish(5, 32, 128, 4, FAKE, FAKE, 1 << 20, None) == INVALID
+    assert lib.maxsim_finish(0, 32, 128, -4, FAKE, FAKE, 1 << 20, None) == INVALID
+    assert lib.maxsim_finish(0, 32, 128, 4, None, FAKE, 1 << 20, None) == INVALID
+    assert lib.maxsim_finish(0, 32, 100, 4, FAKE, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert lib.maxsim_finish(0, 32, 128, 4, FAKE, None, 1 << 20, None) == WORKSPACE
+    assert lib.maxsim_finish(0, 32, 128, 0, None, None, 0, None) == OK
     n = ctypes.c_size_t(0)
     assert lib.maxsim_workspace_size(32, 128, -1, ctypes.byref(n)) == INVALID
     assert lib.maxsim_workspace_size(32, 128, 10, None) == INVALID

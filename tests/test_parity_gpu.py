@@ -86,7 +86,8 @@ SHAPES = [
     # (Lq, d, stride)
     (1, 128, 128), (15, 128, 136), (16, 64, 64), (17, 96, 96), (37, 96, 104), (32, 128, 128),
     (128, 128, 128), (129, 128, 128), (200, 128, 136), (256, 256, 256), (64, 256, 264),
-    (33, 8, 8), (20, 40, 48), (45, 200, 208), (7, 160, 160), (100, 32, 32),
+    (33, 8, 8), (20, 40, 48), (45, 200, 208), (7, 160, 160), (100, 32, 32), (200, 200, 200),
+    (129, 256, 256),
 ]
 
 
@@ -234,6 +235,7 @@ def test_staged_api_matches_one_shot_on_a_side_stream():
     with torch.cuda.stream(side):
         lir.maxsim_plan(offs, lens, w.Lq, w.d, ws)
         got = lir.maxsim_score(Q, X, offs, lens, ws)
+        lir.maxsim_finish(Q, w.B, ws, got)
     torch.cuda.synchronize()
     assert torch.equal(got, ref)
 
