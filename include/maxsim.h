@@ -102,8 +102,8 @@ MAXSIM_API const char *maxsim_status_string(int status);
  *   *bytes. Queries the current device: MAXSIM_ERR_HIP without one.
  *
  * maxsim_plan: the length-binned doc schedule. Reads doc_offsets and doc_lengths and
- *   writes the schedule into `workspace` (two kernel launches). The workspace must be
- *   256-byte aligned and at least maxsim_workspace_size bytes.
+ *   writes the schedule into `workspace` (one kernel launch when B <= 1024, else two).
+ *   The workspace must be 256-byte aligned and at least maxsim_workspace_size bytes.
  *
  * maxsim_score: the score kernel (one launch). Writes the score of every doc the
  *   schedule kept whole; for docs it split into several work items (long docs, when

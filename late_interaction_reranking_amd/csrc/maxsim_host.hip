@@ -84,10 +84,13 @@ plan_count_kernel(const int32_t *__restrict__ lengths, int32_t B, uint32_t docs_
     if (threadIdx.x == kNumBins + 1) row[kNumBins + 1] = (uint32_t)(tiles >> 32);
 }
 
+// With a single plan block (B <= kPlanBlock docs), the scatter kernel counts its own
+// docs (self_count) and the count kernel is not launched.
 __global__ void __launch_bounds__(kPlanBlock)
 plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restrict__ lengths,
                     int32_t B, uint32_t docs_per_block, const uint32_t *__restrict__ hist,
-                    uint32_t nblocks, Header *__restrict__ hdr, DocDesc *__restrict__ desc)
+                    uint32_t nblocks, int self_count, Header *__restrict__ hdr,
+                    DocDesc *__restrict__ desc)
 {
     constexpr int kRowGroups = kPlanBlock / kHistStride;  // 32
     __shared__ unsigned long long part_tot[kRowGroups][kHistStride];
@@ -95,6 +98,23 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
     __shared__ uint32_t bin_next[kNumBins];  // next free slot of each bin for this block
     __shared__ uint32_t wave_cnt[kPlanBlock / kWave][kNumBins];
 
+    if (self_count) {
+        // One block holds every doc: bin counts and tile total straight from lengths.
+        if (threadIdx.x < kHistStride) {
+            part_tot[0][threadIdx.x] = 0;
+            part_before[0][threadIdx.x] = 0;
+        }
+        __syncthreads();
+        unsigned long long my_tiles = 0;
+        for (int64_t i = threadIdx.x; i < (int64_t)B; i += kPlanBlock) {
+            const uint32_t nt = tiles_of(lengths[i]);
+            atomicAdd(&part_tot[0][bin_of(nt)], 1ull);
+            my_tiles += nt;
+        }
+        for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
+        if ((threadIdx.x & (kWave - 1)) == 0) atomicAdd(&part_tot[0][kNumBins], my_tiles);
+        __syncthreads();
+    } else {
     // Column c of the hist table summed over all blocks, and over blocks before ours.
     {
         const int c = threadIdx.x % kHistStride;
@@ -122,6 +142,7 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
         part_before[0][c] = before;
     }
     __syncthreads();
+    }
     if (threadIdx.x == 0) {
         uint32_t start = 0;  // bins in descending order
         for (int b = kNumBins - 1; b >= 0; --b) {
@@ -381,11 +402,15 @@ int launch_plan(const int32_t *offsets, const int32_t *lengths, int32_t B, const
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
     Header *hdr = reinterpret_cast<Header *>(ws + L.header);
     DocDesc *desc = reinterpret_cast<DocDesc *>(ws + L.desc);
-    hipLaunchKernelGGL(plan_count_kernel, dim3(L.plan_blocks), dim3(kPlanBlock), 0, stream,
-                       lengths, B, L.docs_per_plan_block, hist);
-    if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_HIP;
+    const int self_count = L.plan_blocks == 1 && (uint32_t)B <= (uint32_t)kPlanBlock;
+    if (!self_count) {
+        hipLaunchKernelGGL(plan_count_kernel, dim3(L.plan_blocks), dim3(kPlanBlock), 0, stream,
+                           lengths, B, L.docs_per_plan_block, hist);
+        if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_HIP;
+    }
     hipLaunchKernelGGL(plan_scatter_kernel, dim3(L.plan_blocks), dim3(kPlanBlock), 0, stream,
-                       offsets, lengths, B, L.docs_per_plan_block, hist, L.plan_blocks, hdr, desc);
+                       offsets, lengths, B, L.docs_per_plan_block, hist, L.plan_blocks, self_count,
+                       hdr, desc);
     if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_HIP;
     return MAXSIM_OK;
 }

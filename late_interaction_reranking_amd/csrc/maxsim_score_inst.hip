@@ -30,7 +30,7 @@ constexpr int min_waves()
 #ifdef MAXSIM_FORCE_MINW
     return MAXSIM_FORCE_MINW;
 #else
-    constexpr int est = 4 * NQT * NKS + 4 * P * NKS + 4 * NKS + 8 * NQT + 56;
+    constexpr int est = 4 * NQT * NKS + 4 * P * NKS + 4 * NKS + 4 * NQT + 48;
     return est <= 128 ? 4 : (est <= 168 ? 3 : (est <= 256 ? 2 : 1));
 #endif
 }

@@ -250,3 +250,56 @@ def test_errors_raise():
     big = torch.zeros((4, 264), dtype=torch.float16, device=DEV)
     with pytest.raises(lir.MaxSimError):
         lir.maxsim_rerank(big[:2, :264].contiguous(), big, offs, lens)
+
+
+def test_graph_replay_tracks_inputs_changed_in_place():
+    """The staged form (caller workspace, no allocation) captured once in a HIP graph and
+    replayed after Q, offsets and lengths change in place: every replay equals an eager
+    run on the same inputs."""
+    _say("[parity] graph capture and replay")
+    w = workloads.custom(37, 96, np.random.default_rng(30).integers(0, 300, size=500), seed=30,
+                         order="shuffled", gap=(1, 9), stride=104)
+    Q, X, offs, lens = upload(w)
+    B = w.B
+    nbytes = lir.maxsim_workspace_size(w.Lq, w.d, B)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=DEV)
+    out = torch.empty(B, dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):  # warm up (occupancy queries, code loading) before capture
+        lir.maxsim_plan(offs, lens, w.Lq, w.d, ws)
+        lir.maxsim_score(Q, X, offs, lens, ws, scores=out)
+        lir.maxsim_finish(Q, B, ws, out)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        lir.maxsim_plan(offs, lens, w.Lq, w.d, ws)
+        lir.maxsim_score(Q, X, offs, lens, ws, scores=out)
+        lir.maxsim_finish(Q, B, ws, out)
+    rng = np.random.default_rng(31)
+    for it in range(4):
+        if it:
+            Q.copy_(Q[torch.from_numpy(rng.permutation(w.Lq)).to(DEV)])
+            perm = torch.from_numpy(rng.permutation(B)).to(DEV)
+            new_offs, new_lens = offs[perm].clone(), lens[perm].clone()
+            new_lens[: B // 4] = torch.clamp(new_lens[: B // 4] // 2, min=0)
+            offs.copy_(new_offs)
+            lens.copy_(new_lens)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref = lir.rerank(Q, X, offs, lens)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref), f"replay {it}"
+
+
+def test_more_than_a_million_docs():
+    """B past 2^20 makes each plan block take several rounds of 1024 docs."""
+    _say("[parity] 1.1 M docs")
+    B = 1_100_000
+    lengths = np.random.default_rng(32).integers(0, 4, size=B)
+    w = workloads.custom(4, 32, lengths, seed=32, order="shuffled")
+    got = gpu_scores(w)
+    sample = np.random.default_rng(33).choice(B, 20000, replace=False)
+    sample = np.unique(np.concatenate([sample, [0, B - 1], np.nonzero(lengths == 0)[0][:50]]))
+    assert_parity(got[sample], oracle.maxsim_workload(w, docs=sample), "1.1 M docs")
