@@ -69,9 +69,21 @@ def algorithmic_bytes(w) -> int:
     return w.doc_tokens * 2 * w.d + w.B * 12 + w.Lq * w.d * 2
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(w, budget_s: float = 12.0):
     """The oracle, unchanged, on the host cores: whole docs in doc order until the time
-    budget is spent (or all docs are done)."""
+    budget is spent (or all docs are done). Returns the record and the oracle's scores
+    of the docs it scored (doc ids 0 .. n-1)."""
     import numpy as np
 
     import oracle
@@ -80,23 +92,48 @@ def cpu_baseline(w, budget_s: float = 12.0):
     oracle.maxsim_workload(w, docs=np.arange(min(8, w.B)), threads=threads)  # load + warm
     done_docs = 0
     tokens = 0
+    parts = []
     t0 = time.perf_counter()
     batch = 256
     while done_docs < w.B and time.perf_counter() - t0 < budget_s:
         ids = np.arange(done_docs, min(w.B, done_docs + batch))
-        oracle.maxsim_workload(w, docs=ids, threads=threads)
+        parts.append(oracle.maxsim_workload(w, docs=ids, threads=threads))
         tokens += int(w.lengths[ids].astype(np.int64).sum())
         done_docs += len(ids)
         batch = min(batch * 2, 8192)
     dt = time.perf_counter() - t0
-    return {
+    rec = {
         "value": tokens / dt,
         "unit": "doc tokens/s",
         "cores": threads,
         "kind": "oracle",
         "sample": f"first {done_docs} of {w.B} docs ({tokens} doc tokens) of the same "
                   f"workload, fp64 oracle, {dt:.1f} s wall",
+        "cpu_model": cpu_model(),
     }
+    return rec, (np.concatenate(parts) if parts else np.zeros(0))
+
+
+def parity_summary(gpu, ref, B):
+    """Scores of the timed run against the oracle, under the acceptance rule
+    |gpu - oracle| <= 1e-3 (1 + |oracle|); the top-10 check needs every doc scored."""
+    import numpy as np
+
+    n = len(ref)
+    g = np.asarray(gpu[:n], np.float64)
+    inf = np.isinf(ref)
+    fin = ~inf
+    err = np.abs(g[fin] - ref[fin]) / (1.0 + np.abs(ref[fin]))
+    bad = int(np.sum(~(err <= 1e-3))) + int(np.sum(g[inf] != ref[inf]))
+    out = {"docs_checked": int(n), "max_scaled_err": float(err.max()) if err.size else 0.0,
+           "violations": bad, "top10_ok": None}
+    if n == B:
+        order_ref = np.lexsort((np.arange(n), -ref))[:10]
+        order_gpu = np.lexsort((np.arange(n), -g))[:10]
+        want = ref[order_ref]
+        mine = ref[order_gpu]
+        out["top10_ok"] = bool(np.all(np.abs(mine - want) <= 1e-3 * (1 + np.abs(want))))
+    return out
 
 
 def main() -> int:
@@ -221,10 +258,12 @@ def main() -> int:
             "avg_launch_ms": score_avg_ms,
         },
         "cpu_baseline": None,
+        "parity": None,
     }
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        rec["cpu_baseline"] = cpu_baseline(w)
+        rec["cpu_baseline"], ref = cpu_baseline(w)
+        rec["parity"] = parity_summary(scores.cpu().numpy(), ref, w.B)
     print(json.dumps(rec), flush=True)
     return 0
 
