@@ -88,6 +88,43 @@ MAXSIM_API int maxsim_rerank_bf16(const void *Q, int32_t Lq, int32_t d,
                        const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
                        float *scores, void *stream);
 
+/*
+ * Many queries in one launch ("pairs": each doc is scored against its own query).
+ * The Flash-MaxSim rerank page (docs.vllm.ai, vllm.v1.pool.flash_maxsim.
+ * flash_maxsim_rerank, kernel section `_maxsim_rerank_kernel`) refers to a pairs
+ * kernel that widens doc offsets to 64 bits the same way, without showing it; this is
+ * that batch form of the operation above, read as: doc i, with query
+ * j = doc_query[i], gets
+ *
+ *     scores[i] = sum over q < q_lengths[j] of  max over t < doc_lengths[i] of
+ *                 Qs[q_offsets[j] + q] . row(doc_offsets[i] + t)
+ *
+ * Qs:        [q_rows, d] row-major, contiguous: the rows of every query (device).
+ * q_offsets, q_lengths: int32 [nq] (device): query j is rows
+ *            [q_offsets[j], q_offsets[j] + q_lengths[j]) of Qs. Queries may overlap or
+ *            share rows, and a query may be empty (its docs score 0).
+ * max_lq:    an upper bound on q_lengths, 0 <= max_lq <= 256; it picks the kernel
+ *            configuration, so a tight bound is faster.
+ * doc_query: int32 [B] (device): the query of each doc; docs of one query need not
+ *            be adjacent.
+ * Other arguments as for maxsim_rerank. A doc whose query index is outside [0, nq),
+ * or whose query has a negative offset or length, is longer than max_lq or reaches
+ * past row q_rows, gets NaN (these are checked on the device, per doc). Each doc's
+ * score equals the one maxsim_rerank gives for that query alone.
+ */
+MAXSIM_API int maxsim_rerank_pairs(const void *Qs, int32_t q_rows, int32_t d,
+                        const int32_t *q_offsets, const int32_t *q_lengths, int32_t nq,
+                        int32_t max_lq, const void *docs, int64_t stride,
+                        const int32_t *doc_offsets, const int32_t *doc_lengths,
+                        const int32_t *doc_query, int32_t B, float *scores, void *stream);
+
+/* Same as maxsim_rerank_pairs, bf16 Qs and docs. */
+MAXSIM_API int maxsim_rerank_pairs_bf16(const void *Qs, int32_t q_rows, int32_t d,
+                             const int32_t *q_offsets, const int32_t *q_lengths, int32_t nq,
+                             int32_t max_lq, const void *docs, int64_t stride,
+                             const int32_t *doc_offsets, const int32_t *doc_lengths,
+                             const int32_t *doc_query, int32_t B, float *scores, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 MAXSIM_API const char *maxsim_status_string(int status);
 
@@ -120,6 +157,20 @@ MAXSIM_API int maxsim_workspace_size(int32_t Lq, int32_t d, int32_t B, size_t *b
 MAXSIM_API int maxsim_plan(const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
                 int32_t Lq, int32_t d,
                 void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * maxsim_plan_pairs: the schedule of a multi-query batch (the operation of
+ *   maxsim_rerank_pairs, same argument meanings). Size the workspace with
+ *   maxsim_workspace_size(max_lq, d, B); then call maxsim_score and maxsim_finish with
+ *   Q = Qs and Lq = max_lq. Here max_lq must be at least 1 (MAXSIM_ERR_INVALID_ARG
+ *   otherwise; 1 is a valid bound when every query is empty), because maxsim_score and
+ *   maxsim_finish with Lq = 0 write zeros without reading a plan.
+ */
+MAXSIM_API int maxsim_plan_pairs(const int32_t *doc_offsets, const int32_t *doc_lengths,
+                      const int32_t *doc_query, int32_t B,
+                      const int32_t *q_offsets, const int32_t *q_lengths, int32_t nq,
+                      int32_t q_rows, int32_t max_lq, int32_t d,
+                      void *workspace, size_t workspace_bytes, void *stream);
 
 MAXSIM_API int maxsim_score(int dtype, const void *Q, int32_t Lq, int32_t d,
                  const void *docs, int64_t stride,

@@ -4,6 +4,8 @@ One query Q[Lq, d] is scored against B variable-length documents read in place f
 packed, possibly scattered row tensor by per-document (offset, length) pairs:
 score_i = sum over query rows of the best dot product with any of document i's rows
 (Flash-MaxSim rerank page, docs.vllm.ai, vllm.v1.pool.flash_maxsim.flash_maxsim_rerank).
+The pairs entry points score a batch of many queries in one launch, each document
+against its own query.
 
 The computation lives in libmaxsim.so (hand-written HIP, C ABI in include/maxsim.h);
 this package is its ctypes binding. Build the library with
@@ -17,12 +19,16 @@ from .maxsim import (  # noqa: F401
     library_path,
     load,
     maxsim_plan,
+    maxsim_plan_pairs,
     maxsim_rerank,
     maxsim_rerank_bf16,
+    maxsim_rerank_pairs,
+    maxsim_rerank_pairs_bf16,
     maxsim_finish,
     maxsim_score,
     maxsim_status_string,
     maxsim_version,
     maxsim_workspace_size,
     rerank,
+    rerank_pairs,
 )

@@ -36,13 +36,18 @@ constexpr int kMinChunkTiles = 2;
 struct Header {
     unsigned long long total_tiles;          // sum over docs of ceil(len / 16)
     uint32_t bin_count[kNumBins];            // docs per bin
+    uint32_t multi_query;                    // docs carry their own queries (no Q staging)
 };
 
 struct alignas(16) DocDesc {
-    int32_t doc;     // index into scores
-    int32_t offset;  // first row in docs
-    int32_t length;  // rows
-    int32_t tiles;   // ceil(length / 16)
+    int32_t doc;       // index into scores
+    int32_t offset;    // first row in docs
+    int32_t length;    // rows
+    int32_t tiles;     // ceil(length / 16)
+    int32_t query;     // query the doc is scored against
+    int32_t q_offset;  // its first row in Q
+    int32_t q_length;  // its rows; -1 marks an invalid query (the doc's score is NaN)
+    int32_t reserved;
 };
 
 __host__ __device__ inline int bin_of(uint32_t nt)
@@ -85,15 +90,16 @@ inline Layout make_layout(int lq_pad, int32_t B, uint32_t waves_max)
 
 // ---------------------------------------------------------------- score kernel
 struct ScoreArgs {
-    const uint16_t *Q;        // [Lq, d]
+    const uint16_t *Q;        // query rows [*, d]: one query, or several back to back
     const char *docs;         // row r at docs + r * stride_bytes
     int64_t stride_bytes;
     const Header *hdr;
     const DocDesc *desc;
     float *partials;          // [partial_slots, lq_pad]
     float *scores;
-    int32_t Lq, d, ngroups, lq_pad;
-    int32_t q_in_lds;         // Q staged in LDS (else fragments come from global)
+    int32_t Lq;               // rows of the one query staged in LDS (when q_in_lds)
+    int32_t d, ngroups, lq_pad;
+    int32_t q_in_lds;         // LDS holds room for the Q tile; used unless the plan is multi-query
 };
 
 // Q is staged in LDS when its padded tile takes at most this many bytes; a larger
@@ -108,7 +114,19 @@ struct CombineArgs {
     const float *partials;
     float *scores;
     uint32_t score_waves;     // W of the score launch (fixes the chunking)
-    int32_t Lq, nqt, ngroups, lq_pad;
+    int32_t nqt, ngroups, lq_pad;
+};
+
+// What the plan kernels need to know about the queries. A single query is nq = 1 with
+// doc_query, q_offsets and q_lengths null and Lq rows.
+struct QueryTable {
+    const int32_t *doc_query;  // [B] query of each doc (null: all query 0)
+    const int32_t *q_offsets;  // [nq] first row of each query in Q (null: 0)
+    const int32_t *q_lengths;  // [nq] rows of each query (null: Lq)
+    int32_t nq;
+    int32_t q_rows;            // rows of Q; a query must lie inside them
+    int32_t Lq;                // rows of the single query
+    int32_t max_lq;            // longest query the launch is built for
 };
 
 }  // namespace maxsim

@@ -89,7 +89,7 @@ plan_count_kernel(const int32_t *__restrict__ lengths, int32_t B, uint32_t docs_
 __global__ void __launch_bounds__(kPlanBlock)
 plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restrict__ lengths,
                     int32_t B, uint32_t docs_per_block, const uint32_t *__restrict__ hist,
-                    uint32_t nblocks, int self_count, Header *__restrict__ hdr,
+                    uint32_t nblocks, int self_count, const QueryTable qt, Header *__restrict__ hdr,
                     DocDesc *__restrict__ desc)
 {
     constexpr int kRowGroups = kPlanBlock / kHistStride;  // 32
@@ -152,6 +152,7 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
         if (blockIdx.x == 0) {
             for (int b = 0; b < kNumBins; ++b) hdr->bin_count[b] = (uint32_t)part_tot[0][b];
             hdr->total_tiles = part_tot[0][kNumBins] + (part_tot[0][kNumBins + 1] << 32);
+            hdr->multi_query = qt.doc_query ? 1u : 0u;
         }
     }
     __syncthreads();
@@ -184,6 +185,23 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
             dd.offset = offsets[i];
             dd.length = len > 0 ? len : 0;
             dd.tiles = (int32_t)nt;
+            // The doc's query, checked here once so the score kernel needs no host
+            // check: an index outside [0, nq), rows outside Q or a query longer than
+            // the launch was built for make the doc's score NaN.
+            const int32_t q = qt.doc_query ? qt.doc_query[i] : 0;
+            int32_t q_off = 0, q_len = -1;
+            if (q >= 0 && q < qt.nq) {
+                q_off = qt.q_offsets ? qt.q_offsets[q] : 0;
+                q_len = qt.q_lengths ? qt.q_lengths[q] : qt.Lq;
+                if (q_off < 0 || q_len < 0 || q_len > qt.max_lq || (int64_t)q_off + q_len > qt.q_rows) {
+                    q_off = 0;
+                    q_len = -1;
+                }
+            }
+            dd.query = q;
+            dd.q_offset = q_off;
+            dd.q_length = q_len;
+            dd.reserved = 0;
             desc[slot] = dd;
         }
         __syncthreads();
@@ -245,18 +263,19 @@ combine_kernel(const CombineArgs a)
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const int q_len = a.desc[di].q_length;
             float lane_sum = 0.0f;
             for (int grp = 0; grp < a.ngroups; ++grp)
                 for (int qt = 0; qt < a.nqt; ++qt)
                     for (int i = 0; i < 4; ++i) {
                         const int q = (grp * a.nqt + qt) * kTileRows + kgroup * 4 + i;
-                        lane_sum += q < a.Lq ? s_part[0][q] : 0.0f;
+                        lane_sum += q < q_len ? s_part[0][q] : 0.0f;
                     }
             const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 0));
             const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 16));
             const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 32));
             const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 48));
-            if (lane == 0) a.scores[a.desc[di].doc] = ((s0 + s1) + s2) + s3;
+            if (lane == 0) a.scores[a.desc[di].doc] = q_len < 0 ? __builtin_nanf("") : ((s0 + s1) + s2) + s3;
         }
         __syncthreads();
     }
@@ -363,13 +382,18 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t q_lds_bytes(const Config &c) { return (size_t)c.lq_pad * (c.nks * kStepK + 8) * 2; }
 
-// Dynamic LDS of the score kernel: the Q tile (if it fits the budget), then one staging
-// tile per wave, 16 rows of (d/8 | 1) 16-byte chunks, plus one slot that lanes with
-// nothing to stage write.
+// Room for the Q tile is reserved whenever the padded tile fits the budget, so the
+// score kernel's occupancy (and the chunking derived from it) does not depend on the
+// plan; under a multi-query plan the kernel reads each wave's current query from
+// global memory (L2-resident) instead of staging one.
+bool q_staged(const Config &c) { return q_lds_bytes(c) <= kMaxQLdsBytes; }
+
+// Dynamic LDS of the score kernel: the Q tile (if it fits), then one staging tile per
+// wave, 16 rows of (d/8 | 1) 16-byte chunks, plus one slot that lanes with nothing to
+// stage write.
 size_t score_lds_bytes(const Config &c, int32_t d)
 {
-    const size_t q = q_lds_bytes(c);
-    return (q <= kMaxQLdsBytes ? q : 0) + (size_t)kScoreWaves * (kTileRows * ((d / 8) | 1) + 1) * 16;
+    return (q_staged(c) ? q_lds_bytes(c) : 0) + (size_t)kScoreWaves * (kTileRows * ((d / 8) | 1) + 1) * 16;
 }
 
 int check_common(const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
@@ -396,8 +420,22 @@ int workspace_layout(int32_t Lq, int32_t d, int32_t B, Layout *L)
     return MAXSIM_OK;
 }
 
+// The query table of a launch over one query of Lq rows: every doc takes query 0.
+QueryTable single_query(int32_t Lq)
+{
+    QueryTable qt;
+    qt.doc_query = nullptr;
+    qt.q_offsets = nullptr;
+    qt.q_lengths = nullptr;
+    qt.nq = 1;
+    qt.q_rows = Lq;
+    qt.Lq = Lq;
+    qt.max_lq = Lq;
+    return qt;
+}
+
 int launch_plan(const int32_t *offsets, const int32_t *lengths, int32_t B, const Layout &L,
-                char *ws, hipStream_t stream)
+                const QueryTable &qt, char *ws, hipStream_t stream)
 {
     uint32_t *hist = reinterpret_cast<uint32_t *>(ws + L.hist);
     Header *hdr = reinterpret_cast<Header *>(ws + L.header);
@@ -410,7 +448,7 @@ int launch_plan(const int32_t *offsets, const int32_t *lengths, int32_t B, const
     }
     hipLaunchKernelGGL(plan_scatter_kernel, dim3(L.plan_blocks), dim3(kPlanBlock), 0, stream,
                        offsets, lengths, B, L.docs_per_plan_block, hist, L.plan_blocks, self_count,
-                       hdr, desc);
+                       qt, hdr, desc);
     if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_HIP;
     return MAXSIM_OK;
 }
@@ -422,15 +460,16 @@ int launch_fill(float *scores, int32_t B, float v, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
 }
 
+// Lq: rows of the one query, or the longest query of a multi-query plan.
 int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
-                 int32_t B, float *scores, const Layout &L, char *ws, hipStream_t stream)
+                 float *scores, const Layout &L, char *ws, hipStream_t stream)
 {
     const Config c = choose_config(Lq, d);
     if (c.lq_pad > kMaxLqPad || c.nqt * c.nks > kMaxFragsPerGroup) return MAXSIM_ERR_UNSUPPORTED;
     const void *fn = dtype == MAXSIM_BF16 ? maxsim_score_kernel_bf16(c.nks, c.nqt)
                                           : maxsim_score_kernel_f16(c.nks, c.nqt);
     if (!fn) return MAXSIM_ERR_UNSUPPORTED;
-    const bool q_in_lds = q_lds_bytes(c) <= kMaxQLdsBytes;
+    const bool q_in_lds = q_staged(c);
     const size_t lds = score_lds_bytes(c, d);
     int per_cu = 0;
     if (score_blocks_per_cu(fn, lds, &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
@@ -475,12 +514,29 @@ int launch_finish(int dtype, int32_t Lq, int32_t d, float *scores, const Layout 
     ca.partials = reinterpret_cast<const float *>(ws + L.partials);
     ca.scores = scores;
     ca.score_waves = (uint32_t)(f.cus * per_cu * kScoreWaves);
-    ca.Lq = Lq;
     ca.nqt = c.nqt;
     ca.ngroups = c.ngroups;
     ca.lq_pad = c.lq_pad;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)f.cus * 4u), dim3(kScoreBlock), 0, stream, ca);
     return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
+}
+
+// Plan, score and combine with a stream-ordered temporary workspace; qt.max_lq sizes
+// the kernel configuration.
+int run_all(int dtype, const void *Q, const QueryTable &qt, int32_t d, const void *docs,
+            int64_t stride, const int32_t *offsets, const int32_t *lengths, int32_t B, float *scores,
+            hipStream_t stream)
+{
+    Layout L;
+    if (workspace_layout(qt.max_lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    void *ws = nullptr;
+    if (hipMallocAsync(&ws, L.total, stream) != hipSuccess) return MAXSIM_ERR_HIP;
+    char *w = static_cast<char *>(ws);
+    int rc = launch_plan(offsets, lengths, B, L, qt, w, stream);
+    if (rc == MAXSIM_OK) rc = launch_score(dtype, Q, qt.max_lq, d, docs, stride, scores, L, w, stream);
+    if (rc == MAXSIM_OK) rc = launch_finish(dtype, qt.max_lq, d, scores, L, w, stream);
+    if (hipFreeAsync(ws, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
+    return rc;
 }
 
 int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
@@ -491,16 +547,40 @@ int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, in
     if (B == 0) return MAXSIM_OK;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     if (Lq == 0) return launch_fill(scores, B, 0.0f, stream);
-    Layout L;
-    if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
-    void *ws = nullptr;
-    if (hipMallocAsync(&ws, L.total, stream) != hipSuccess) return MAXSIM_ERR_HIP;
-    int rc = launch_plan(offsets, lengths, B, L, static_cast<char *>(ws), stream);
-    if (rc == MAXSIM_OK)
-        rc = launch_score(dtype, Q, Lq, d, docs, stride, B, scores, L, static_cast<char *>(ws), stream);
-    if (rc == MAXSIM_OK) rc = launch_finish(dtype, Lq, d, scores, L, static_cast<char *>(ws), stream);
-    if (hipFreeAsync(ws, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
-    return rc;
+    return run_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, stream);
+}
+
+// Host checks of a query table (the per-doc checks run in the plan kernel).
+int check_queries(const int32_t *q_offsets, const int32_t *q_lengths, int32_t nq, int32_t q_rows,
+                  int32_t max_lq, const int32_t *doc_query, int32_t B, QueryTable *qt)
+{
+    if (q_rows < 0 || nq < 0 || max_lq < 0) return MAXSIM_ERR_INVALID_ARG;
+    if (max_lq > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
+    if (B > 0 && (!doc_query || (nq > 0 && (!q_offsets || !q_lengths)))) return MAXSIM_ERR_INVALID_ARG;
+    if (((uintptr_t)doc_query | (uintptr_t)q_offsets | (uintptr_t)q_lengths) & 3u) return MAXSIM_ERR_INVALID_ARG;
+    qt->doc_query = doc_query;
+    qt->q_offsets = q_offsets;
+    qt->q_lengths = q_lengths;
+    qt->nq = nq;
+    qt->q_rows = q_rows;
+    qt->Lq = 0;
+    qt->max_lq = max_lq;
+    return MAXSIM_OK;
+}
+
+int rerank_pairs(int dtype, const void *Qs, int32_t q_rows, int32_t d, const int32_t *q_offsets,
+                 const int32_t *q_lengths, int32_t nq, int32_t max_lq, const void *docs, int64_t stride,
+                 const int32_t *offsets, const int32_t *lengths, const int32_t *doc_query, int32_t B,
+                 float *scores, void *stream_ptr)
+{
+    QueryTable qt;
+    int st = check_queries(q_offsets, q_lengths, nq, q_rows, max_lq, doc_query, B, &qt);
+    if (st != MAXSIM_OK) return st;
+    st = check_common(Qs, max_lq, d, docs, stride, offsets, lengths, B, scores);
+    if (st != MAXSIM_OK) return st;
+    if (B == 0) return MAXSIM_OK;
+    return run_all(dtype, Qs, qt, d, docs, stride, offsets, lengths, B, scores,
+                   static_cast<hipStream_t>(stream_ptr));
 }
 
 }  // namespace
@@ -519,6 +599,24 @@ int maxsim_rerank_bf16(const void *Q, int32_t Lq, int32_t d, const void *docs, i
                        float *scores, void *stream)
 {
     return rerank(MAXSIM_BF16, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores, stream);
+}
+
+int maxsim_rerank_pairs(const void *Qs, int32_t q_rows, int32_t d, const int32_t *q_offsets,
+                        const int32_t *q_lengths, int32_t nq, int32_t max_lq, const void *docs,
+                        int64_t stride, const int32_t *doc_offsets, const int32_t *doc_lengths,
+                        const int32_t *doc_query, int32_t B, float *scores, void *stream)
+{
+    return rerank_pairs(MAXSIM_F16, Qs, q_rows, d, q_offsets, q_lengths, nq, max_lq, docs, stride,
+                        doc_offsets, doc_lengths, doc_query, B, scores, stream);
+}
+
+int maxsim_rerank_pairs_bf16(const void *Qs, int32_t q_rows, int32_t d, const int32_t *q_offsets,
+                             const int32_t *q_lengths, int32_t nq, int32_t max_lq, const void *docs,
+                             int64_t stride, const int32_t *doc_offsets, const int32_t *doc_lengths,
+                             const int32_t *doc_query, int32_t B, float *scores, void *stream)
+{
+    return rerank_pairs(MAXSIM_BF16, Qs, q_rows, d, q_offsets, q_lengths, nq, max_lq, docs, stride,
+                        doc_offsets, doc_lengths, doc_query, B, scores, stream);
 }
 
 const char *maxsim_status_string(int status)
@@ -554,7 +652,30 @@ int maxsim_plan(const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t 
     Layout L;
     if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
-    return launch_plan(doc_offsets, doc_lengths, B, L, static_cast<char *>(workspace),
+    return launch_plan(doc_offsets, doc_lengths, B, L, single_query(Lq), static_cast<char *>(workspace),
+                       static_cast<hipStream_t>(stream));
+}
+
+int maxsim_plan_pairs(const int32_t *doc_offsets, const int32_t *doc_lengths, const int32_t *doc_query,
+                      int32_t B, const int32_t *q_offsets, const int32_t *q_lengths, int32_t nq,
+                      int32_t q_rows, int32_t max_lq, int32_t d, void *workspace, size_t workspace_bytes,
+                      void *stream)
+{
+    if (B < 0 || d < 1) return MAXSIM_ERR_INVALID_ARG;
+    if (B > 0 && (!doc_offsets || !doc_lengths)) return MAXSIM_ERR_INVALID_ARG;
+    QueryTable qt;
+    const int st = check_queries(q_offsets, q_lengths, nq, q_rows, max_lq, doc_query, B, &qt);
+    if (st != MAXSIM_OK) return st;
+    if (d > kMaxD || d % 8 != 0) return MAXSIM_ERR_UNSUPPORTED;
+    // maxsim_score and maxsim_finish take Lq = 0 to mean "no query rows at all" and
+    // write zeros without reading a plan, which would hide invalid queries.
+    if (max_lq < 1) return MAXSIM_ERR_INVALID_ARG;
+    if (B == 0) return MAXSIM_OK;
+    if (!workspace || ((uintptr_t)workspace & 255u)) return MAXSIM_ERR_WORKSPACE;
+    Layout L;
+    if (workspace_layout(max_lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
+    return launch_plan(doc_offsets, doc_lengths, B, L, qt, static_cast<char *>(workspace),
                        static_cast<hipStream_t>(stream));
 }
 
@@ -572,7 +693,7 @@ int maxsim_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     Layout L;
     if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
-    return launch_score(dtype, Q, Lq, d, docs, stride, B, scores, L, static_cast<char *>(workspace), s);
+    return launch_score(dtype, Q, Lq, d, docs, stride, scores, L, static_cast<char *>(workspace), s);
 }
 
 int maxsim_finish(int dtype, int32_t Lq, int32_t d, int32_t B, float *scores, void *workspace,

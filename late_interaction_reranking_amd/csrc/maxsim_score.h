@@ -43,6 +43,9 @@
 //     end) starts at -inf instead of 0, which keeps it at -inf; then an element-wise
 //     running max per lane; at the end of the item four DPP row_ror steps
 //     (8, 4, 2, 1) take the max over the 16 doc-row lanes.
+//   - Several queries may share a launch, each doc scored against its own (the
+//     descriptor carries the query's rows); a wave reloads its query fragments only
+//     when the query changes between its items.
 //   - Query rows past Lq (zero padding) are masked to 0 and the per-row maxima are
 //     summed in one fixed order (ascending query tile, then j, then the four lane
 //     groups), whether the doc was scored in one item or several, so scores do not
@@ -132,8 +135,10 @@ score_kernel(const ScoreArgs a)
     const uint32_t W = gridDim.x * kScoreWaves;
     const uint32_t wid = blockIdx.x * kScoreWaves + wave;
 
-    // ---- stage Q (zero-padded) into LDS
-    if (a.q_in_lds) {
+    // ---- stage Q (zero-padded) into LDS: one query, when its tile fits; under a
+    // multi-query plan every wave reads its current query from global memory.
+    const bool stage_q = a.q_in_lds && a.hdr->multi_query == 0u;
+    if (stage_q) {
         constexpr int CPR = DPAD / 8;  // 16-byte chunks per padded row
         const int n = lq_pad * CPR;
         for (int e = threadIdx.x; e < n; e += kScoreBlock) {
@@ -175,25 +180,27 @@ score_kernel(const ScoreArgs a)
     // K-step NKS-1 may hold 8-column chunks past d: those fragment lanes are zero.
     const bool last_chunk_ok = (NKS - 1) * 4 + kgroup < C;
 
+    // Query fragments of register group grp for the query at rows [q_off, q_off + q_len)
+    // of Q: from LDS when the one query is staged there, else from global memory.
     u32x4 qf[NQT][NKS];
-    auto load_q = [&](int grp) {
+    auto load_q = [&](int grp, int q_off, int q_len) {
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
             for (int s = 0; s < NKS; ++s) {
                 const int row = (grp * NQT + qt) * kTileRows + row_in_tile;
                 const int col = (s * 4 + kgroup) * 8;
-                if (a.q_in_lds) {
+                if (stage_q) {
                     qf[qt][s] = *reinterpret_cast<const u32x4 *>(qs + row * LDQ + col);
                 } else {
                     u32x4 v = {0u, 0u, 0u, 0u};
-                    if (row < Lq && col < a.d)
-                        v = *reinterpret_cast<const u32x4 *>(a.Q + (size_t)row * a.d + col);
+                    if (row < q_len && col < a.d)
+                        v = *reinterpret_cast<const u32x4 *>(a.Q + ((size_t)q_off + row) * a.d + col);
                     qf[qt][s] = v;
                 }
             }
     };
-    if (ngroups == 1) load_q(0);
+    int loaded_query = -1;  // query whose fragments qf holds (one register group only)
 
     // ---- the wave's items: round r deals item r W + w to wave w (r even) or to wave
     // W-1-w (r odd)
@@ -207,6 +214,9 @@ score_kernel(const ScoreArgs a)
         int doc;
         uint32_t K;      // chunks of its doc (1: the item is the whole doc)
         uint32_t g;      // claim index (slot of its partial maxima when K > 1)
+        int query;       // its doc's query: rows [q_off, q_off + q_len) of Q
+        int q_off;
+        int q_len;       // -1: invalid query, the doc's score is NaN
         bool valid;
     };
     auto fetch = [&](uint32_t g, Item &it, DocDesc &dd) {
@@ -222,10 +232,14 @@ score_kernel(const ScoreArgs a)
         if (!sp.valid) {
             sp.base = (uint64_t)(uintptr_t)a.docs;
             sp.nrows = sp.ntiles = sp.doc = 0;
+            sp.query = sp.q_off = sp.q_len = 0;
             sp.K = 1;
             return sp;
         }
         sp.doc = (int)wave_uniform((uint32_t)dd.doc);
+        sp.query = (int)wave_uniform((uint32_t)dd.query);
+        sp.q_off = (int)wave_uniform((uint32_t)dd.q_offset);
+        sp.q_len = (int)wave_uniform((uint32_t)dd.q_length);
         const int64_t off = (int64_t)(int32_t)wave_uniform((uint32_t)dd.offset);
         const int len = (int)wave_uniform((uint32_t)dd.length);
         const uint32_t nt = wave_uniform((uint32_t)dd.tiles);
@@ -311,7 +325,10 @@ score_kernel(const ScoreArgs a)
             g2 = claim_of(r++);
             fetch(g2, i2, d2);
         }
-        if (ngroups > 1) load_q(grp);
+        if (ngroups > 1 || cur.query != loaded_query) {
+            load_q(grp, cur.q_off, cur.q_len);
+            loaded_query = ngroups > 1 ? -1 : cur.query;
+        }
         // Everything that steers the tile loop is wave-uniform; restate it so that it
         // stays in scalar registers (the loads' descriptors are built from it).
         const bool more_groups = grp + 1 < ngroups;
@@ -357,7 +374,7 @@ score_kernel(const ScoreArgs a)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int q = (grp * NQT + qt) * kTileRows + kgroup * 4 + i;
-                    lane_sum += q < Lq ? rmax[qt][i] : 0.0f;
+                    lane_sum += q < cur.q_len ? rmax[qt][i] : 0.0f;
                 }
         } else if (row_in_tile == 0) {
 #pragma unroll
@@ -378,7 +395,7 @@ score_kernel(const ScoreArgs a)
             const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 16));
             const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 32));
             const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
-            if (lane == 0) a.scores[cur.doc] = ((s0 + s1) + s2) + s3;
+            if (lane == 0) a.scores[cur.doc] = cur.q_len < 0 ? __builtin_nanf("") : ((s0 + s1) + s2) + s3;
         }
         // (split docs: the combine kernel finishes them)
         lane_sum = 0.0f;

@@ -12,6 +12,13 @@ The functions carry the C ABI's names (include/maxsim.h) and take torch tensors:
     maxsim_finish(Q, B, workspace, scores)
     rerank(...)  picks maxsim_rerank or maxsim_rerank_bf16 from Q's dtype
 
+    maxsim_rerank_pairs(Qs, q_offsets, q_lengths, max_lq, docs, doc_offsets,
+                        doc_lengths, doc_query)                 fp16, many queries
+    maxsim_rerank_pairs_bf16(...)                               bf16, many queries
+    maxsim_plan_pairs(doc_offsets, doc_lengths, doc_query, q_offsets, q_lengths,
+                      q_rows, max_lq, d, workspace)
+    rerank_pairs(...)  picks the fp16 or bf16 pairs entry from Qs's dtype
+
 Q is [Lq, d] and contiguous; docs is a 2-D view whose rows are docs.stride(0) elements
 apart with unit column stride (a column slice of a wider tensor works: its extra
 columns are never read); doc_offsets and doc_lengths are int32 [B] on the same device.
@@ -40,6 +47,10 @@ __all__ = [
     "maxsim_finish",
     "maxsim_version",
     "rerank",
+    "maxsim_rerank_pairs",
+    "maxsim_rerank_pairs_bf16",
+    "maxsim_plan_pairs",
+    "rerank_pairs",
     "MAXSIM_F16",
     "MAXSIM_BF16",
 ]
@@ -91,6 +102,13 @@ def load() -> ctypes.CDLL:
         lib.maxsim_score.argtypes = [ctypes.c_int, P, I32, I32, P, I64, P, P, I32, P, P, SZ, P]
         lib.maxsim_finish.restype = ctypes.c_int
         lib.maxsim_finish.argtypes = [ctypes.c_int, I32, I32, I32, P, P, SZ, P]
+        pr = [P, I32, I32, P, P, I32, I32, P, I64, P, P, P, I32, P, P]
+        for name in ("maxsim_rerank_pairs", "maxsim_rerank_pairs_bf16"):
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = pr
+        lib.maxsim_plan_pairs.restype = ctypes.c_int
+        lib.maxsim_plan_pairs.argtypes = [P, P, P, I32, P, P, I32, I32, I32, I32, P, SZ, P]
         lib.maxsim_version.restype = ctypes.c_int
         lib.maxsim_version.argtypes = []
         _lib = lib
@@ -197,11 +215,14 @@ def maxsim_plan(doc_offsets, doc_lengths, Lq: int, d: int, workspace: torch.Tens
     _check(st, "maxsim_plan")
 
 
-def maxsim_score(Q, docs, doc_offsets, doc_lengths, workspace: torch.Tensor, scores=None) -> torch.Tensor:
-    """Enqueue the score kernel over a schedule maxsim_plan wrote into `workspace`.
-    Docs the schedule split are completed by maxsim_finish."""
+def maxsim_score(Q, docs, doc_offsets, doc_lengths, workspace: torch.Tensor, scores=None,
+                 Lq: int | None = None) -> torch.Tensor:
+    """Enqueue the score kernel over a schedule maxsim_plan (or maxsim_plan_pairs) wrote
+    into `workspace`. Docs the schedule split are completed by maxsim_finish. Lq
+    defaults to Q's row count; after maxsim_plan_pairs pass its max_lq."""
     dtype = torch.bfloat16 if Q.dtype == torch.bfloat16 else torch.float16
-    Lq, d, stride, B = _marshal(Q, docs, doc_offsets, doc_lengths, dtype)
+    q_rows, d, stride, B = _marshal(Q, docs, doc_offsets, doc_lengths, dtype)
+    Lq = q_rows if Lq is None else int(Lq)
     if scores is None:
         scores = torch.empty(B, dtype=torch.float32, device=docs.device)
     ptr, nbytes = _ws(workspace)
@@ -214,9 +235,10 @@ def maxsim_score(Q, docs, doc_offsets, doc_lengths, workspace: torch.Tensor, sco
     return scores
 
 
-def maxsim_finish(Q, B: int, workspace: torch.Tensor, scores: torch.Tensor) -> torch.Tensor:
+def maxsim_finish(Q, B: int, workspace: torch.Tensor, scores: torch.Tensor,
+                  Lq: int | None = None) -> torch.Tensor:
     """Enqueue the combine step: the scores of docs the schedule split into several
-    work items. Q only supplies Lq, d and the element format."""
+    work items. Q only supplies d, the element format and, unless given, Lq."""
     if Q.dim() != 2:
         raise ValueError("Q must be 2-D")
     if scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
@@ -224,7 +246,80 @@ def maxsim_finish(Q, B: int, workspace: torch.Tensor, scores: torch.Tensor) -> t
     code = MAXSIM_BF16 if Q.dtype == torch.bfloat16 else MAXSIM_F16
     ptr, nbytes = _ws(workspace)
     with torch.cuda.device(workspace.device):
-        st = load().maxsim_finish(code, int(Q.shape[0]), int(Q.shape[1]), int(B), scores.data_ptr(),
+        st = load().maxsim_finish(code, int(Q.shape[0]) if Lq is None else int(Lq), int(Q.shape[1]),
+                                  int(B), scores.data_ptr(),
                                   ptr, nbytes, _stream(workspace))
     _check(st, "maxsim_finish")
     return scores
+
+
+def _int32_vec(t, name, dev):
+    if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous():
+        raise TypeError(f"{name} must be a contiguous 1-D int32 tensor")
+    if t.device != dev:
+        raise ValueError(f"{name} must live on the GPU, with docs")
+
+
+def _rerank_pairs(fn_name, dtype, Qs, q_offsets, q_lengths, max_lq, docs, doc_offsets, doc_lengths,
+                  doc_query, scores=None):
+    _, d, stride, B = _marshal(Qs, docs, doc_offsets, doc_lengths, dtype)
+    dev = docs.device
+    for name, t in (("q_offsets", q_offsets), ("q_lengths", q_lengths), ("doc_query", doc_query)):
+        _int32_vec(t, name, dev)
+    if q_offsets.shape != q_lengths.shape:
+        raise ValueError("q_offsets and q_lengths must have one entry per query")
+    if doc_query.shape[0] != B:
+        raise ValueError("doc_query must have one entry per doc")
+    if scores is None:
+        scores = torch.empty(B, dtype=torch.float32, device=dev)
+    elif scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    with torch.cuda.device(dev):
+        st = getattr(load(), fn_name)(
+            Qs.data_ptr(), int(Qs.shape[0]), d, q_offsets.data_ptr(), q_lengths.data_ptr(),
+            int(q_offsets.shape[0]), int(max_lq), docs.data_ptr(), stride, doc_offsets.data_ptr(),
+            doc_lengths.data_ptr(), doc_query.data_ptr(), B, scores.data_ptr(), _stream(docs),
+        )
+    _check(st, fn_name)
+    return scores
+
+
+def maxsim_rerank_pairs(Qs, q_offsets, q_lengths, max_lq: int, docs, doc_offsets, doc_lengths,
+                        doc_query, scores=None) -> torch.Tensor:
+    """fp32 [B] scores, doc i against query doc_query[i] (rows q_offsets[j] ..
+    q_offsets[j] + q_lengths[j] - 1 of Qs); fp16 inputs. max_lq bounds q_lengths."""
+    return _rerank_pairs("maxsim_rerank_pairs", torch.float16, Qs, q_offsets, q_lengths, max_lq,
+                         docs, doc_offsets, doc_lengths, doc_query, scores)
+
+
+def maxsim_rerank_pairs_bf16(Qs, q_offsets, q_lengths, max_lq: int, docs, doc_offsets, doc_lengths,
+                             doc_query, scores=None) -> torch.Tensor:
+    """maxsim_rerank_pairs with bf16 inputs."""
+    return _rerank_pairs("maxsim_rerank_pairs_bf16", torch.bfloat16, Qs, q_offsets, q_lengths, max_lq,
+                         docs, doc_offsets, doc_lengths, doc_query, scores)
+
+
+def rerank_pairs(Qs, q_offsets, q_lengths, max_lq: int, docs, doc_offsets, doc_lengths, doc_query,
+                 scores=None) -> torch.Tensor:
+    """maxsim_rerank_pairs or maxsim_rerank_pairs_bf16, chosen by Qs's dtype."""
+    fn = maxsim_rerank_pairs_bf16 if Qs.dtype == torch.bfloat16 else maxsim_rerank_pairs
+    return fn(Qs, q_offsets, q_lengths, max_lq, docs, doc_offsets, doc_lengths, doc_query, scores)
+
+
+def maxsim_plan_pairs(doc_offsets, doc_lengths, doc_query, q_offsets, q_lengths, q_rows: int,
+                      max_lq: int, d: int, workspace: torch.Tensor) -> None:
+    """Enqueue the schedule of a multi-query batch into `workspace`, sized by
+    maxsim_workspace_size(max_lq, d, B). The batch is then scored by
+    maxsim_score(Qs, ..., Lq=max_lq) and maxsim_finish(Qs, B, workspace, scores,
+    Lq=max_lq). max_lq must be at least 1."""
+    dev = workspace.device
+    for name, t in (("doc_offsets", doc_offsets), ("doc_lengths", doc_lengths), ("doc_query", doc_query),
+                    ("q_offsets", q_offsets), ("q_lengths", q_lengths)):
+        _int32_vec(t, name, dev)
+    ptr, nbytes = _ws(workspace)
+    with torch.cuda.device(dev):
+        st = load().maxsim_plan_pairs(doc_offsets.data_ptr(), doc_lengths.data_ptr(), doc_query.data_ptr(),
+                                      int(doc_offsets.shape[0]), q_offsets.data_ptr(), q_lengths.data_ptr(),
+                                      int(q_offsets.shape[0]), int(q_rows), int(max_lq), int(d), ptr, nbytes,
+                                      _stream(workspace))
+    _check(st, "maxsim_plan_pairs")

@@ -19,6 +19,12 @@ tests/test_oracle_golden.py and tests/test_oracle_mutants.py):
   scaling), the empty-doc / empty-query special cases, and by hand-worked golden
   examples. A mutation test plants plausible mistakes in a copy of the C source and
   checks that the pins catch each one.
+- ``maxsim_pairs(...)``: the batch form with several queries, each doc scored against
+  its own query. The pages name a pairs kernel without defining it; the reading taken
+  is that doc i's score is the single-query score above for query doc_query[i], and a
+  doc whose query index or rows are invalid scores NaN. Written as that selection plus
+  ``maxsim``. Pinned by exact brute force per doc on tiny batches with interleaved,
+  repeated, empty and invalid queries (tests/test_oracle_pairs.py).
 """
 
 from __future__ import annotations
@@ -30,7 +36,8 @@ import threading
 
 import numpy as np
 
-__all__ = ["FMT", "build", "Oracle", "decode", "maxsim", "maxsim_workload", "max_threads"]
+__all__ = ["FMT", "build", "Oracle", "decode", "maxsim", "maxsim_pairs", "maxsim_workload",
+           "max_threads"]
 
 FMT = {"f16": 0, "bf16": 1}
 
@@ -138,12 +145,46 @@ def maxsim(fmt, Q, X, offsets, lengths, d=None, threads: int = 0) -> np.ndarray:
     return _get().maxsim(fmt, Q, X, offsets, lengths, d=d, threads=threads)
 
 
+def maxsim_pairs(fmt, Qs, q_offsets, q_lengths, X, offsets, lengths, doc_query, max_lq,
+                 d=None, threads: int = 0) -> np.ndarray:
+    """fp64 scores of docs that each take their own query.
+
+    Query j is rows [q_offsets[j], q_offsets[j] + q_lengths[j]) of Qs (uint16 bits,
+    [q_rows, d]); doc i is scored, as by ``maxsim``, against query doc_query[i]. A doc
+    gets NaN when its query index is outside [0, nq) or that query has a negative
+    offset or length, more than max_lq rows, or rows past the end of Qs.
+    """
+    Qs = np.ascontiguousarray(Qs, dtype=np.uint16)
+    d = Qs.shape[1] if d is None else int(d)
+    q_offsets = np.asarray(q_offsets, np.int64)
+    q_lengths = np.asarray(q_lengths, np.int64)
+    offsets = np.asarray(offsets, np.int64)
+    lengths = np.asarray(lengths, np.int64)
+    doc_query = np.asarray(doc_query, np.int64)
+    nq, q_rows = q_offsets.shape[0], Qs.shape[0]
+    out = np.full(offsets.shape[0], np.nan)
+    for j in np.unique(doc_query):
+        if not 0 <= j < nq:
+            continue
+        lo, n = int(q_offsets[j]), int(q_lengths[j])
+        if lo < 0 or n < 0 or n > max_lq or lo + n > q_rows:
+            continue
+        sel = np.nonzero(doc_query == j)[0]
+        out[sel] = maxsim(fmt, Qs[lo:lo + n], X, offsets[sel], lengths[sel], d=d, threads=threads)
+    return out
+
+
 def maxsim_workload(w, docs=None, threads: int = 0) -> np.ndarray:
     """fp64 scores of a workloads.Workload, for all docs or for the doc ids `docs`."""
     offs, lens = w.offsets, w.lengths
+    dq = w.doc_query
     if docs is not None:
         docs = np.asarray(docs, dtype=np.int64)
         offs, lens = offs[docs], lens[docs]
+        dq = None if dq is None else dq[docs]
+    if dq is not None:
+        return maxsim_pairs(w.dtype, w.Q, w.q_offsets, w.q_lengths, w.X, offs, lens, dq, w.Lq,
+                            d=w.d, threads=threads)
     return maxsim(w.dtype, w.Q, w.X, offs, lens, d=w.d, threads=threads)
 
 

@@ -32,7 +32,8 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     for n in ("maxsim_rerank", "maxsim_rerank_bf16", "maxsim_status_string",
               "maxsim_workspace_size", "maxsim_plan", "maxsim_score", "maxsim_finish",
-              "maxsim_version"):
+              "maxsim_version", "maxsim_rerank_pairs", "maxsim_rerank_pairs_bf16",
+              "maxsim_plan_pairs"):
         assert n in names
 
 
@@ -116,3 +117,51 @@ def test_staged_validation(lib):
     assert lib.maxsim_workspace_size(32, 128, 10, None) == INVALID
     assert lib.maxsim_workspace_size(32, 100, 10, ctypes.byref(n)) == UNSUPPORTED
     del P
+
+
+def call_pairs(lib, fn="maxsim_rerank_pairs", Qs=FAKE, q_rows=64, d=128, qo=FAKE + 8192,
+               ql=FAKE + 12288, nq=4, max_lq=32, docs=FAKE, stride=128, offs=FAKE,
+               lens=FAKE + 1024, dq=FAKE + 16384, B=10, scores=FAKE + 4096):
+    return getattr(lib, fn)(Qs, q_rows, d, qo, ql, nq, max_lq, docs, stride, offs, lens, dq, B,
+                            scores, None)
+
+
+@pytest.mark.parametrize("fn", ["maxsim_rerank_pairs", "maxsim_rerank_pairs_bf16"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(nq=-1), INVALID),
+    (dict(q_rows=-1), INVALID),
+    (dict(max_lq=-1), INVALID),
+    (dict(max_lq=257), UNSUPPORTED),
+    (dict(dq=None), INVALID),
+    (dict(qo=None), INVALID),
+    (dict(ql=None), INVALID),
+    (dict(dq=FAKE + 2), INVALID),
+    (dict(qo=FAKE + 1), INVALID),
+    (dict(Qs=None), INVALID),
+    (dict(Qs=FAKE + 4), UNSUPPORTED),
+    (dict(d=12, stride=16), UNSUPPORTED),
+    (dict(stride=64), INVALID),
+    (dict(docs=None), INVALID),
+    (dict(scores=None), INVALID),
+    (dict(B=-3), INVALID),
+    (dict(nq=0, qo=None, ql=None, B=0, docs=None, offs=None, lens=None, dq=None, scores=None), OK),
+    (dict(B=0), OK),
+])
+def test_pairs_host_validation(lib, fn, kw, code):
+    assert call_pairs(lib, fn, **kw) == code
+
+
+def test_plan_pairs_validation(lib):
+    def plan(offs=FAKE, lens=FAKE, dq=FAKE, B=4, qo=FAKE, ql=FAKE, nq=2, q_rows=40, max_lq=32, d=128,
+             ws=FAKE, nbytes=1 << 20):
+        return lib.maxsim_plan_pairs(offs, lens, dq, B, qo, ql, nq, q_rows, max_lq, d, ws, nbytes, None)
+
+    assert plan(max_lq=0) == INVALID        # staged score/finish read Lq = 0 as "no rows"
+    assert plan(max_lq=257) == UNSUPPORTED
+    assert plan(dq=None) == INVALID
+    assert plan(offs=None) == INVALID
+    assert plan(nq=-1) == INVALID
+    assert plan(d=100) == UNSUPPORTED
+    assert plan(ws=None) == WORKSPACE
+    assert plan(ws=FAKE + 128) == WORKSPACE
+    assert plan(B=0, offs=None, lens=None, dq=None, ws=None) == OK

@@ -38,6 +38,8 @@ __all__ = [
     "long_doc",
     "scattered",
     "large",
+    "pairs",
+    "custom_pairs",
     "round_f16",
     "round_bf16",
     "F16_NAN",
@@ -67,10 +69,24 @@ class Workload:
     seed: int = 0
     planted: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
     notes: str = ""
+    # Several queries in one batch (None: one query, Q itself). Query j is rows
+    # [q_offsets[j], q_offsets[j] + q_lengths[j]) of Q; doc i takes query doc_query[i];
+    # Lq is then the longest query.
+    q_offsets: np.ndarray | None = None  # int32 [nq]
+    q_lengths: np.ndarray | None = None  # int32 [nq]
+    doc_query: np.ndarray | None = None  # int32 [B]
 
     @property
     def B(self) -> int:
         return int(self.offsets.shape[0])
+
+    @property
+    def multi_query(self) -> bool:
+        return self.doc_query is not None
+
+    @property
+    def nq(self) -> int:
+        return 1 if self.q_offsets is None else int(self.q_offsets.shape[0])
 
     @property
     def T(self) -> int:
@@ -325,15 +341,75 @@ def _plant(w: Workload, frac: float, noise: float) -> None:
     w.planted = docs.astype(np.int64)
 
 
+def custom_pairs(
+    q_lengths,
+    d: int,
+    docs_per_query,
+    doc_lengths,
+    *,
+    dtype: str = "f16",
+    seed: int = 0,
+    interleave: bool = False,
+    name: str = "custom_pairs",
+    **kw,
+) -> Workload:
+    """A batch of several queries, each with its own docs.
+
+    q_lengths[j]: rows of query j (its rows follow query j-1's in Q).
+    docs_per_query[j]: docs of query j; doc_lengths: one length per doc, in doc order.
+    Docs are numbered query by query (all of query 0's, then query 1's, ...), unless
+    interleave, which shuffles the doc -> query assignment. Other keywords go to
+    custom() and shape the doc-row tensor.
+    """
+    q_lengths = np.asarray(q_lengths, dtype=np.int64)
+    docs_per_query = np.asarray(docs_per_query, dtype=np.int64)
+    if q_lengths.shape != docs_per_query.shape:
+        raise ValueError("one docs_per_query entry per query")
+    w = custom(0, d, doc_lengths, dtype=dtype, seed=seed, name=name, **kw)
+    if int(docs_per_query.sum()) != w.B:
+        raise ValueError("docs_per_query must sum to the number of docs")
+    doc_query = np.repeat(np.arange(q_lengths.shape[0]), docs_per_query)
+    if interleave:
+        doc_query = np.random.default_rng([seed, _S_META, 2]).permutation(doc_query)
+    q_offsets = np.concatenate([[0], np.cumsum(q_lengths)[:-1]]) if q_lengths.size else q_lengths
+    rows = int(q_lengths.sum())
+    qrng = np.random.default_rng([seed, _S_Q])
+    w.Q = _round(_unit_rows(qrng, rows, d), dtype) if rows else np.zeros((0, d), np.uint16)
+    w.Lq = int(q_lengths.max()) if q_lengths.size else 0
+    w.q_offsets = q_offsets.astype(np.int32)
+    w.q_lengths = q_lengths.astype(np.int32)
+    w.doc_query = doc_query.astype(np.int32)
+    return w
+
+
+def pairs(seed: int = 5, **kw) -> Workload:
+    """A serving batch of 64 queries with lengths U[16,32], each with 1000 ColBERT-
+    shaped docs (lengths U[64,300]), d 128, fp16: 64,000 docs, ~11.3 M rows packed
+    query by query, each query's docs in a random memory order."""
+    meta = np.random.default_rng([seed, _S_META, 0])
+    nq, per = 64, 1000
+    q_lengths = meta.integers(16, 32, size=nq, endpoint=True)
+    lengths = meta.integers(64, 300, size=nq * per, endpoint=True)
+    perm = np.concatenate([j * per + meta.permutation(per) for j in range(nq)])
+    w = custom_pairs(q_lengths, 128, np.full(nq, per), lengths, dtype="f16", seed=seed,
+                     name="pairs", **kw)
+    # Re-lay docs so that each query's docs sit together in memory, shuffled within.
+    offsets, T = _layout(w.lengths.astype(np.int64), perm, np.zeros(nq * per - 1, np.int64), 0)
+    assert T == w.T
+    w.offsets = offsets.astype(np.int32)
+    return w
+
+
 CONFIGS = {
     "tiny": tiny,
     "colbert": colbert,
     "long_doc": long_doc,
     "scattered": scattered,
     "large": large,
+    "pairs": pairs,
 }
 
 
 def make(name: str, **kw) -> Workload:
-    """Build one of the five named workloads."""
+    """Build one of the named workloads."""
     return CONFIGS[name](**kw)
