@@ -125,6 +125,34 @@ MAXSIM_API int maxsim_rerank_pairs_bf16(const void *Qs, int32_t q_rows, int32_t 
                              const int32_t *doc_offsets, const int32_t *doc_lengths,
                              const int32_t *doc_query, int32_t B, float *scores, void *stream);
 
+/*
+ * Several queries scored against the same documents, in passes that read each doc
+ * tile once for all the queries of a pass. Prior art for reading a tile once per group
+ * of query rows: the request-segmented QSA scorer page (ReVolta pull request 59,
+ * "Change" section), which multiplies each loaded key tile by the rows of one request
+ * together. The operation is maxsim_rerank's, once per query:
+ *
+ *     scores[j * B + i] = MaxSim score of query j against doc i
+ *
+ * Qs:        [sum of q_lengths, d] (device): the queries' rows back to back, query j
+ *            starting right after query j-1; contiguous, 16-byte aligned.
+ * q_lengths: int32 [nq], a HOST array: rows of each query, 0 <= q_lengths[j] <= 256 (an
+ *            empty query scores 0 against every doc). Read during the call only.
+ * scores:    fp32 [nq, B] row-major (device).
+ * Other arguments as for maxsim_rerank. Query j's scores equal, bit for bit, those
+ * maxsim_rerank gives for query j alone. Allocates its workspace stream-ordered.
+ */
+MAXSIM_API int maxsim_rerank_multi(const void *Qs, const int32_t *q_lengths, int32_t nq, int32_t d,
+                        const void *docs, int64_t stride,
+                        const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                        float *scores, void *stream);
+
+/* Same as maxsim_rerank_multi, bf16 Qs and docs. */
+MAXSIM_API int maxsim_rerank_multi_bf16(const void *Qs, const int32_t *q_lengths, int32_t nq,
+                             int32_t d, const void *docs, int64_t stride,
+                             const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                             float *scores, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 MAXSIM_API const char *maxsim_status_string(int status);
 

@@ -5,7 +5,8 @@ packed, possibly scattered row tensor by per-document (offset, length) pairs:
 score_i = sum over query rows of the best dot product with any of document i's rows
 (Flash-MaxSim rerank page, docs.vllm.ai, vllm.v1.pool.flash_maxsim.flash_maxsim_rerank).
 The pairs entry points score a batch of many queries in one launch, each document
-against its own query.
+against its own query; the multi entry points score several queries against the same
+documents, reading each document tile once for a pass of up to 128 query rows.
 
 The computation lives in libmaxsim.so (hand-written HIP, C ABI in include/maxsim.h);
 this package is its ctypes binding. Build the library with
@@ -22,6 +23,8 @@ from .maxsim import (  # noqa: F401
     maxsim_plan_pairs,
     maxsim_rerank,
     maxsim_rerank_bf16,
+    maxsim_rerank_multi,
+    maxsim_rerank_multi_bf16,
     maxsim_rerank_pairs,
     maxsim_rerank_pairs_bf16,
     maxsim_finish,
@@ -30,5 +33,6 @@ from .maxsim import (  # noqa: F401
     maxsim_version,
     maxsim_workspace_size,
     rerank,
+    rerank_multi,
     rerank_pairs,
 )

@@ -22,6 +22,8 @@ constexpr int kMaxFragsPerGroup = 32;         // NQT * NKS <= 32 -> <= 128 VGPRs
 // Padded query rows: g groups of ceil(tiles / g) tiles, tiles <= 16, g <= 4 (a group
 // holds >= 4 tiles), so at most tiles + g - 1 <= 19 tiles.
 constexpr int kMaxLqPad = 19 * kTileRows;
+constexpr int kMaxQTiles = kMaxLqPad / kTileRows;
+constexpr uint32_t kNaNBits = 0x7FC00000u;    // fp32 quiet NaN: the score of a doc whose query is invalid
 
 // ---------------------------------------------------------------- schedule
 // Docs are binned by tile count nt = ceil(len / 16): bin 0 holds nt <= 1, bin b >= 1
@@ -89,17 +91,31 @@ inline Layout make_layout(int lq_pad, int32_t B, uint32_t waves_max)
 }
 
 // ---------------------------------------------------------------- score kernel
+// The query rows of one score launch as 16-row query tiles: the one query of a
+// single-query launch, or several queries that score the same docs, each starting on
+// a tile boundary (a tile never mixes two queries, so each query's rows meet the lanes
+// exactly as they would alone). Tile T holds rows src[T] .. src[T] + rows[T] - 1 of Q;
+// ends[T] >= 0 says that tile T is its query's last and gives that query's score row
+// (scores + ends[T] * score_stride). Not used under a multi-query "pairs" plan, whose
+// docs carry their own query rows.
+struct QueryTiles {
+    int64_t score_stride;           // elements between the score rows of two queries
+    uint16_t src[kMaxQTiles];
+    uint8_t rows[kMaxQTiles];       // 0 .. 16
+    int8_t ends[kMaxQTiles];        // score row completed by tile T, or -1
+};
+
 struct ScoreArgs {
-    const uint16_t *Q;        // query rows [*, d]: one query, or several back to back
+    const uint16_t *Q;        // query rows [*, d]
     const char *docs;         // row r at docs + r * stride_bytes
     int64_t stride_bytes;
     const Header *hdr;
     const DocDesc *desc;
     float *partials;          // [partial_slots, lq_pad]
     float *scores;
-    int32_t Lq;               // rows of the one query staged in LDS (when q_in_lds)
     int32_t d, ngroups, lq_pad;
     int32_t q_in_lds;         // LDS holds room for the Q tile; used unless the plan is multi-query
+    QueryTiles qt;
 };
 
 // Q is staged in LDS when its padded tile takes at most this many bytes; a larger
@@ -115,6 +131,7 @@ struct CombineArgs {
     float *scores;
     uint32_t score_waves;     // W of the score launch (fixes the chunking)
     int32_t nqt, ngroups, lq_pad;
+    QueryTiles qt;            // as in ScoreArgs
 };
 
 // What the plan kernels need to know about the queries. A single query is nq = 1 with

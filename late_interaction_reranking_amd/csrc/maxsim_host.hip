@@ -3,6 +3,7 @@
 #include "maxsim.h"
 
 #include <mutex>
+#include <vector>
 
 #include "maxsim_common.h"
 #include "maxsim_sched.h"
@@ -234,6 +235,7 @@ combine_kernel(const CombineArgs a)
     const uint32_t split = tab.split_docs;
     const int kgroup = lane >> 4;
     const int lq_pad = a.lq_pad;
+    const bool pairs = a.hdr->multi_query != 0u;
     for (uint32_t di = blockIdx.x; di < split; di += gridDim.x) {
         const Item it = locate_doc(L, lane, di);
         const float *base = a.partials + (size_t)it.first * lq_pad;
@@ -263,19 +265,38 @@ combine_kernel(const CombineArgs a)
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
             __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            // The score kernel's per-query sums, in its order (query tiles ascending,
+            // lane groups last).
             const int q_len = a.desc[di].q_length;
+            const int doc = a.desc[di].doc;
+            const int ntiles = a.ngroups * a.nqt;
             float lane_sum = 0.0f;
-            for (int grp = 0; grp < a.ngroups; ++grp)
-                for (int qt = 0; qt < a.nqt; ++qt)
-                    for (int i = 0; i < 4; ++i) {
-                        const int q = (grp * a.nqt + qt) * kTileRows + kgroup * 4 + i;
-                        lane_sum += q < q_len ? s_part[0][q] : 0.0f;
-                    }
-            const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 0));
-            const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 16));
-            const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 32));
-            const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, lane_sum), 48));
-            if (lane == 0) a.scores[a.desc[di].doc] = q_len < 0 ? __builtin_nanf("") : ((s0 + s1) + s2) + s3;
+            for (int T = 0; T < ntiles; ++T) {
+                int nr, end;
+                if (pairs) {
+                    const int left = q_len - T * kTileRows;
+                    nr = left < 0 ? 0 : (left > kTileRows ? kTileRows : left);
+                    end = T == ntiles - 1 ? 0 : -1;
+                } else {
+                    nr = a.qt.rows[T];
+                    end = a.qt.ends[T];
+                }
+                for (int i = 0; i < 4; ++i)
+                    lane_sum += kgroup * 4 + i < nr ? s_part[0][T * kTileRows + kgroup * 4 + i] : 0.0f;
+                if (end >= 0) {
+                    const int ls = __builtin_bit_cast(int, lane_sum);
+                    const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 0));
+                    const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 16));
+                    const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 32));
+                    const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
+                    // NaN for an invalid query, chosen and stored as bits (the
+                    // library is compiled without NaN semantics for its max steps).
+                    const uint32_t v = pairs && q_len < 0 ? kNaNBits
+                                                          : __builtin_bit_cast(uint32_t, ((s0 + s1) + s2) + s3);
+                    if (lane == 0) reinterpret_cast<uint32_t *>(a.scores)[(size_t)end * a.qt.score_stride + doc] = v;
+                    lane_sum = 0.0f;
+                }
+            }
         }
         __syncthreads();
     }
@@ -396,11 +417,13 @@ size_t score_lds_bytes(const Config &c, int32_t d)
     return (q_staged(c) ? q_lds_bytes(c) : 0) + (size_t)kScoreWaves * (kTileRows * ((d / 8) | 1) + 1) * 16;
 }
 
+// scores_needed = false: no score is written (zero queries), so scores may be null.
 int check_common(const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
-                 const int32_t *offsets, const int32_t *lengths, int32_t B, const float *scores)
+                 const int32_t *offsets, const int32_t *lengths, int32_t B, const float *scores,
+                 bool scores_needed = true)
 {
     if (B < 0 || Lq < 0 || d < 1 || stride < d) return MAXSIM_ERR_INVALID_ARG;
-    if (B > 0 && (!docs || !offsets || !lengths || !scores)) return MAXSIM_ERR_INVALID_ARG;
+    if (B > 0 && (!docs || !offsets || !lengths || (scores_needed && !scores))) return MAXSIM_ERR_INVALID_ARG;
     if (B > 0 && Lq > 0 && !Q) return MAXSIM_ERR_INVALID_ARG;
     if (d > kMaxD || d % 8 != 0 || Lq > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
     if (stride % 8 != 0 || stride > kMaxStride) return MAXSIM_ERR_UNSUPPORTED;
@@ -460,9 +483,25 @@ int launch_fill(float *scores, int32_t B, float v, hipStream_t stream)
     return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
 }
 
-// Lq: rows of the one query, or the longest query of a multi-query plan.
+// Query tiles of one query of Lq rows, whose scores are one row.
+QueryTiles single_tiles(int32_t Lq)
+{
+    QueryTiles t{};
+    t.score_stride = 0;
+    const int nt = (Lq + kTileRows - 1) / kTileRows;
+    for (int T = 0; T < kMaxQTiles; ++T) {
+        const int left = Lq - T * kTileRows;
+        t.src[T] = (uint16_t)(T < nt ? T * kTileRows : 0);
+        t.rows[T] = (uint8_t)(left <= 0 ? 0 : (left > kTileRows ? kTileRows : left));
+        t.ends[T] = (int8_t)(T == nt - 1 ? 0 : -1);
+    }
+    return t;
+}
+
+// Lq: rows of the one query, the longest query of a pairs plan, or 16 x the query
+// tiles of a launch over several queries sharing the docs (qt describes them).
 int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
-                 float *scores, const Layout &L, char *ws, hipStream_t stream)
+                 float *scores, const Layout &L, char *ws, const QueryTiles &qt, hipStream_t stream)
 {
     const Config c = choose_config(Lq, d);
     if (c.lq_pad > kMaxLqPad || c.nqt * c.nks > kMaxFragsPerGroup) return MAXSIM_ERR_UNSUPPORTED;
@@ -483,11 +522,11 @@ int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     a.desc = reinterpret_cast<const DocDesc *>(ws + L.desc);
     a.partials = reinterpret_cast<float *>(ws + L.partials);
     a.scores = scores;
-    a.Lq = Lq;
     a.d = d;
     a.ngroups = c.ngroups;
     a.lq_pad = c.lq_pad;
     a.q_in_lds = q_in_lds ? 1 : 0;
+    a.qt = qt;
     void *args[] = {&a};
     const dim3 grid((unsigned)(f.cus * per_cu));
     if (hipLaunchKernel(fn, grid, dim3(kScoreBlock), args, lds, stream) != hipSuccess) return MAXSIM_ERR_HIP;
@@ -497,7 +536,7 @@ int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
 // The combine kernel recomputes the score kernel's chunking, which depends on that
 // launch's wave count: the same instance and occupancy are looked up here.
 int launch_finish(int dtype, int32_t Lq, int32_t d, float *scores, const Layout &L, char *ws,
-                  hipStream_t stream)
+                  const QueryTiles &qt, hipStream_t stream)
 {
     const Config c = choose_config(Lq, d);
     if (c.lq_pad > kMaxLqPad || c.nqt * c.nks > kMaxFragsPerGroup) return MAXSIM_ERR_UNSUPPORTED;
@@ -517,6 +556,7 @@ int launch_finish(int dtype, int32_t Lq, int32_t d, float *scores, const Layout 
     ca.nqt = c.nqt;
     ca.ngroups = c.ngroups;
     ca.lq_pad = c.lq_pad;
+    ca.qt = qt;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)f.cus * 4u), dim3(kScoreBlock), 0, stream, ca);
     return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
 }
@@ -532,9 +572,10 @@ int run_all(int dtype, const void *Q, const QueryTable &qt, int32_t d, const voi
     void *ws = nullptr;
     if (hipMallocAsync(&ws, L.total, stream) != hipSuccess) return MAXSIM_ERR_HIP;
     char *w = static_cast<char *>(ws);
+    const QueryTiles tiles = single_tiles(qt.max_lq);  // (a pairs plan ignores them)
     int rc = launch_plan(offsets, lengths, B, L, qt, w, stream);
-    if (rc == MAXSIM_OK) rc = launch_score(dtype, Q, qt.max_lq, d, docs, stride, scores, L, w, stream);
-    if (rc == MAXSIM_OK) rc = launch_finish(dtype, qt.max_lq, d, scores, L, w, stream);
+    if (rc == MAXSIM_OK) rc = launch_score(dtype, Q, qt.max_lq, d, docs, stride, scores, L, w, tiles, stream);
+    if (rc == MAXSIM_OK) rc = launch_finish(dtype, qt.max_lq, d, scores, L, w, tiles, stream);
     if (hipFreeAsync(ws, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
     return rc;
 }
@@ -583,6 +624,108 @@ int rerank_pairs(int dtype, const void *Qs, int32_t q_rows, int32_t d, const int
                    static_cast<hipStream_t>(stream_ptr));
 }
 
+// Several queries against the same docs: the queries (rows back to back in Qs, lengths
+// on the host) are packed in order into passes of at most one register group of query
+// tiles, each query starting on a tile; a query longer than a group has a pass of its
+// own. One plan serves every pass; each pass is one score launch and one combine
+// launch, reading the docs once for all of its queries. Empty queries score 0.
+int rerank_multi(int dtype, const void *Qs, const int32_t *q_lengths, int32_t nq, int32_t d,
+                 const void *docs, int64_t stride, const int32_t *offsets, const int32_t *lengths,
+                 int32_t B, float *scores, void *stream_ptr)
+{
+    if (nq < 0 || (nq > 0 && !q_lengths)) return MAXSIM_ERR_INVALID_ARG;
+    int64_t total_rows = 0;
+    for (int32_t j = 0; j < nq; ++j) {
+        if (q_lengths[j] < 0) return MAXSIM_ERR_INVALID_ARG;
+        if (q_lengths[j] > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
+        total_rows += q_lengths[j];
+    }
+    const int st = check_common(Qs, total_rows > 0 ? 1 : 0, d, docs, stride, offsets, lengths, B, scores, nq > 0);
+    if (st != MAXSIM_OK) return st;
+    if (B == 0 || nq == 0) return MAXSIM_OK;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+
+    struct Pass {
+        int32_t j0, j1;    // queries [j0, j1)
+        int64_t row0;      // first row of query j0 in Qs
+        int tiles;
+    };
+    const int nks = (d + kStepK - 1) / kStepK;
+    int group_tiles = kMaxFragsPerGroup / nks;
+    if (group_tiles > kMaxQTilesPerGroup) group_tiles = kMaxQTilesPerGroup;
+    std::vector<Pass> passes;
+    int max_pad = 0;
+    {
+        int64_t row = 0;
+        Pass cur{0, 0, 0, 0};
+        auto close = [&](int32_t j_end) {
+            if (cur.tiles > 0) {
+                cur.j1 = j_end;
+                passes.push_back(cur);
+                const int pad = choose_config(cur.tiles * kTileRows, d).lq_pad;
+                if (pad > max_pad) max_pad = pad;
+            }
+            cur.tiles = 0;
+        };
+        for (int32_t j = 0; j < nq; ++j) {
+            const int t = (q_lengths[j] + kTileRows - 1) / kTileRows;
+            if (t > 0) {
+                // A new pass when this query does not fit, or when the score row
+                // offset inside the pass would outgrow the table's int8.
+                if (cur.tiles > 0 && (cur.tiles + t > group_tiles || j - cur.j0 > 127)) close(j);
+                if (cur.tiles == 0) {
+                    cur.j0 = j;
+                    cur.row0 = row;
+                }
+                cur.tiles += t;
+                if (cur.tiles >= group_tiles) close(j + 1);
+            }
+            row += q_lengths[j];
+        }
+        close(nq);
+    }
+
+    int rc = MAXSIM_OK;
+    for (int32_t j = 0; j < nq && rc == MAXSIM_OK; ++j)
+        if (q_lengths[j] == 0) rc = launch_fill(scores + (size_t)j * B, B, 0.0f, stream);
+    if (rc != MAXSIM_OK || passes.empty()) return rc;
+
+    DeviceFacts f;
+    if (current_facts(&f) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    const Layout L = make_layout(max_pad, B, (uint32_t)(f.cus * f.waves_per_cu));
+    void *ws = nullptr;
+    if (hipMallocAsync(&ws, L.total, stream) != hipSuccess) return MAXSIM_ERR_HIP;
+    char *w = static_cast<char *>(ws);
+    rc = launch_plan(offsets, lengths, B, L, single_query(0), w, stream);
+    const char *qbytes = static_cast<const char *>(Qs);
+    for (size_t p = 0; p < passes.size() && rc == MAXSIM_OK; ++p) {
+        const Pass &ps = passes[p];
+        QueryTiles qt{};
+        qt.score_stride = B;
+        for (int T = 0; T < kMaxQTiles; ++T) qt.ends[T] = -1;
+        int T = 0;
+        int64_t rel = 0;  // row of query j relative to the pass
+        for (int32_t j = ps.j0; j < ps.j1; ++j) {
+            const int Lj = q_lengths[j];
+            const int t = (Lj + kTileRows - 1) / kTileRows;
+            for (int k = 0; k < t; ++k, ++T) {
+                const int left = Lj - k * kTileRows;
+                qt.src[T] = (uint16_t)(rel + k * kTileRows);
+                qt.rows[T] = (uint8_t)(left > kTileRows ? kTileRows : left);
+                qt.ends[T] = (int8_t)(k == t - 1 ? j - ps.j0 : -1);
+            }
+            rel += Lj;
+        }
+        const void *Qp = qbytes + (size_t)ps.row0 * (size_t)d * 2;
+        float *sp = scores + (size_t)ps.j0 * (size_t)B;
+        const int rows = ps.tiles * kTileRows;
+        rc = launch_score(dtype, Qp, rows, d, docs, stride, sp, L, w, qt, stream);
+        if (rc == MAXSIM_OK) rc = launch_finish(dtype, rows, d, sp, L, w, qt, stream);
+    }
+    if (hipFreeAsync(ws, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
+    return rc;
+}
+
 }  // namespace
 
 extern "C" {
@@ -617,6 +760,22 @@ int maxsim_rerank_pairs_bf16(const void *Qs, int32_t q_rows, int32_t d, const in
 {
     return rerank_pairs(MAXSIM_BF16, Qs, q_rows, d, q_offsets, q_lengths, nq, max_lq, docs, stride,
                         doc_offsets, doc_lengths, doc_query, B, scores, stream);
+}
+
+int maxsim_rerank_multi(const void *Qs, const int32_t *q_lengths, int32_t nq, int32_t d, const void *docs,
+                        int64_t stride, const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                        float *scores, void *stream)
+{
+    return rerank_multi(MAXSIM_F16, Qs, q_lengths, nq, d, docs, stride, doc_offsets, doc_lengths, B, scores,
+                        stream);
+}
+
+int maxsim_rerank_multi_bf16(const void *Qs, const int32_t *q_lengths, int32_t nq, int32_t d,
+                             const void *docs, int64_t stride, const int32_t *doc_offsets,
+                             const int32_t *doc_lengths, int32_t B, float *scores, void *stream)
+{
+    return rerank_multi(MAXSIM_BF16, Qs, q_lengths, nq, d, docs, stride, doc_offsets, doc_lengths, B, scores,
+                        stream);
 }
 
 const char *maxsim_status_string(int status)
@@ -693,7 +852,8 @@ int maxsim_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     Layout L;
     if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
-    return launch_score(dtype, Q, Lq, d, docs, stride, scores, L, static_cast<char *>(workspace), s);
+    return launch_score(dtype, Q, Lq, d, docs, stride, scores, L, static_cast<char *>(workspace),
+                        single_tiles(Lq), s);
 }
 
 int maxsim_finish(int dtype, int32_t Lq, int32_t d, int32_t B, float *scores, void *workspace,
@@ -709,7 +869,7 @@ int maxsim_finish(int dtype, int32_t Lq, int32_t d, int32_t B, float *scores, vo
     Layout L;
     if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
-    return launch_finish(dtype, Lq, d, scores, L, static_cast<char *>(workspace),
+    return launch_finish(dtype, Lq, d, scores, L, static_cast<char *>(workspace), single_tiles(Lq),
                          static_cast<hipStream_t>(stream));
 }
 

@@ -43,13 +43,17 @@
 //     end) starts at -inf instead of 0, which keeps it at -inf; then an element-wise
 //     running max per lane; at the end of the item four DPP row_ror steps
 //     (8, 4, 2, 1) take the max over the 16 doc-row lanes.
-//   - Several queries may share a launch, each doc scored against its own (the
-//     descriptor carries the query's rows); a wave reloads its query fragments only
-//     when the query changes between its items.
-//   - Query rows past Lq (zero padding) are masked to 0 and the per-row maxima are
-//     summed in one fixed order (ascending query tile, then j, then the four lane
-//     groups), whether the doc was scored in one item or several, so scores do not
-//     depend on how the schedule chunked the doc.
+//   - Several queries may score the same docs in one launch: their rows are stacked,
+//     each query starting on a 16-row tile, so every doc tile is loaded once and
+//     multiplied by all of them; a table of query tiles says where each query ends.
+//   - Or several queries may share a launch with each doc scored against its own (a
+//     "pairs" plan: the descriptor carries the query's rows); a wave then reloads its
+//     query fragments only when the query changes between its items.
+//   - Query rows past their query's end (zero padding) are masked to 0 and each
+//     query's per-row maxima are summed in one fixed order (ascending query tile, then
+//     j, then the four lane groups), whether the doc was scored in one item or several,
+//     so scores do not depend on how the schedule chunked the doc, nor on which other
+//     queries shared the launch.
 //   - A doc split into K chunks: each chunk writes its per-row maxima to its own slot
 //     with plain stores; the combine kernel, launched next on the same stream, takes
 //     the max over the K slots (exact, so order-free) and does the same fixed-order
@@ -128,25 +132,27 @@ score_kernel(const ScoreArgs a)
     __shared__ BinTables tab;
 
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
-    const int Lq = a.Lq;
+    const int wave = (int)wave_uniform(threadIdx.x / kWave);  // uniform: claims and descriptors stay scalar
     const int lq_pad = a.lq_pad;
     const int ngroups = a.ngroups;
     const uint32_t W = gridDim.x * kScoreWaves;
     const uint32_t wid = blockIdx.x * kScoreWaves + wave;
 
-    // ---- stage Q (zero-padded) into LDS: one query, when its tile fits; under a
-    // multi-query plan every wave reads its current query from global memory.
-    const bool stage_q = a.q_in_lds && a.hdr->multi_query == 0u;
+    // ---- stage the query tiles (zero-padded) into LDS when they fit; under a
+    // multi-query "pairs" plan every wave reads its current query from global memory.
+    const bool pairs = a.hdr->multi_query != 0u;
+    const bool stage_q = a.q_in_lds && !pairs;
     if (stage_q) {
         constexpr int CPR = DPAD / 8;  // 16-byte chunks per padded row
         const int n = lq_pad * CPR;
         for (int e = threadIdx.x; e < n; e += kScoreBlock) {
             const int r = e / CPR;
             const int c = e - r * CPR;
+            const int T = r / kTileRows;
+            const int ri = r - T * kTileRows;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (r < Lq && c * 8 < a.d)
-                v = *reinterpret_cast<const u32x4 *>(a.Q + (size_t)r * a.d + c * 8);
+            if (ri < (int)a.qt.rows[T] && c * 8 < a.d)
+                v = *reinterpret_cast<const u32x4 *>(a.Q + ((size_t)a.qt.src[T] + ri) * a.d + c * 8);
             *reinterpret_cast<u32x4 *>(qs + r * LDQ + c * 8) = v;
         }
     }
@@ -180,25 +186,29 @@ score_kernel(const ScoreArgs a)
     // K-step NKS-1 may hold 8-column chunks past d: those fragment lanes are zero.
     const bool last_chunk_ok = (NKS - 1) * 4 + kgroup < C;
 
-    // Query fragments of register group grp for the query at rows [q_off, q_off + q_len)
-    // of Q: from LDS when the one query is staged there, else from global memory.
+    // Query fragments of register group grp: from LDS when the query tiles are staged
+    // there, else from global memory, by the tile table or, under a pairs plan, for the
+    // item's query at rows [q_off, q_off + q_len) of Q.
     u32x4 qf[NQT][NKS];
     auto load_q = [&](int grp, int q_off, int q_len) {
 #pragma unroll
-        for (int qt = 0; qt < NQT; ++qt)
+        for (int qt = 0; qt < NQT; ++qt) {
+            const int T = grp * NQT + qt;
+            const int row = T * kTileRows + row_in_tile;
+            const bool row_ok = pairs ? row < q_len : row_in_tile < (int)a.qt.rows[T];
+            const size_t src = pairs ? (size_t)q_off + row : (size_t)a.qt.src[T] + row_in_tile;
 #pragma unroll
             for (int s = 0; s < NKS; ++s) {
-                const int row = (grp * NQT + qt) * kTileRows + row_in_tile;
                 const int col = (s * 4 + kgroup) * 8;
                 if (stage_q) {
                     qf[qt][s] = *reinterpret_cast<const u32x4 *>(qs + row * LDQ + col);
                 } else {
                     u32x4 v = {0u, 0u, 0u, 0u};
-                    if (row < q_len && col < a.d)
-                        v = *reinterpret_cast<const u32x4 *>(a.Q + ((size_t)q_off + row) * a.d + col);
+                    if (row_ok && col < a.d) v = *reinterpret_cast<const u32x4 *>(a.Q + src * a.d + col);
                     qf[qt][s] = v;
                 }
             }
+        }
     };
     int loaded_query = -1;  // query whose fragments qf holds (one register group only)
 
@@ -369,13 +379,39 @@ score_kernel(const ScoreArgs a)
             for (int i = 0; i < 4; ++i) rmax[qt][i] = row16_max(rmax[qt][i]);
 
         if (cur.K == 1) {
+            // Rows past the end of their query add nothing; each query's sum is stored
+            // at its last tile: lanes add their rows in ascending order, then the four
+            // lane groups in a fixed order.
 #pragma unroll
-            for (int qt = 0; qt < NQT; ++qt)
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int q = (grp * NQT + qt) * kTileRows + kgroup * 4 + i;
-                    lane_sum += q < cur.q_len ? rmax[qt][i] : 0.0f;
+            for (int qt = 0; qt < NQT; ++qt) {
+                const int T = grp * NQT + qt;
+                int nr, end;
+                if (pairs) {
+                    const int left = cur.q_len - T * kTileRows;
+                    nr = left < 0 ? 0 : (left > kTileRows ? kTileRows : left);
+                    end = T == ngroups * NQT - 1 ? 0 : -1;
+                } else {
+                    nr = a.qt.rows[T];
+                    end = a.qt.ends[T];
                 }
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lane_sum += kgroup * 4 + i < nr ? rmax[qt][i] : 0.0f;
+                if (end >= 0) {
+                    const int ls = __builtin_bit_cast(int, lane_sum);
+                    const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 0));
+                    const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 16));
+                    const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 32));
+                    const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
+                    // NaN for an invalid query, chosen and stored as bits (this code is
+                    // compiled without NaN semantics for its max steps).
+                    const uint32_t v = pairs && cur.q_len < 0
+                                           ? kNaNBits
+                                           : __builtin_bit_cast(uint32_t, ((s0 + s1) + s2) + s3);
+                    if (lane == 0)
+                        reinterpret_cast<uint32_t *>(a.scores)[(size_t)end * a.qt.score_stride + cur.doc] = v;
+                    lane_sum = 0.0f;
+                }
+            }
         } else if (row_in_tile == 0) {
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
@@ -387,15 +423,6 @@ score_kernel(const ScoreArgs a)
         if (more_groups) {
             ++grp;
             continue;
-        }
-        if (cur.K == 1) {
-            // Fixed-order sum over the four lane groups.
-            const int ls = __builtin_bit_cast(int, lane_sum);
-            const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 0));
-            const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 16));
-            const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 32));
-            const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
-            if (lane == 0) a.scores[cur.doc] = cur.q_len < 0 ? __builtin_nanf("") : ((s0 + s1) + s2) + s3;
         }
         // (split docs: the combine kernel finishes them)
         lane_sum = 0.0f;

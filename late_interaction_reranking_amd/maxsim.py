@@ -19,6 +19,11 @@ The functions carry the C ABI's names (include/maxsim.h) and take torch tensors:
                       q_rows, max_lq, d, workspace)
     rerank_pairs(...)  picks the fp16 or bf16 pairs entry from Qs's dtype
 
+    maxsim_rerank_multi(Qs, q_lengths, docs, doc_offsets, doc_lengths)
+                       fp16, several queries against the same docs -> [nq, B]
+    maxsim_rerank_multi_bf16(...)                               bf16
+    rerank_multi(...)  picks one of the two from Qs's dtype
+
 Q is [Lq, d] and contiguous; docs is a 2-D view whose rows are docs.stride(0) elements
 apart with unit column stride (a column slice of a wider tensor works: its extra
 columns are never read); doc_offsets and doc_lengths are int32 [B] on the same device.
@@ -51,6 +56,9 @@ __all__ = [
     "maxsim_rerank_pairs_bf16",
     "maxsim_plan_pairs",
     "rerank_pairs",
+    "maxsim_rerank_multi",
+    "maxsim_rerank_multi_bf16",
+    "rerank_multi",
     "MAXSIM_F16",
     "MAXSIM_BF16",
 ]
@@ -107,6 +115,11 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = pr
+        mr = [P, P, I32, I32, P, I64, P, P, I32, P, P]
+        for name in ("maxsim_rerank_multi", "maxsim_rerank_multi_bf16"):
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = mr
         lib.maxsim_plan_pairs.restype = ctypes.c_int
         lib.maxsim_plan_pairs.argtypes = [P, P, P, I32, P, P, I32, I32, I32, I32, P, SZ, P]
         lib.maxsim_version.restype = ctypes.c_int
@@ -323,3 +336,43 @@ def maxsim_plan_pairs(doc_offsets, doc_lengths, doc_query, q_offsets, q_lengths,
                                       int(q_offsets.shape[0]), int(q_rows), int(max_lq), int(d), ptr, nbytes,
                                       _stream(workspace))
     _check(st, "maxsim_plan_pairs")
+
+
+def _rerank_multi(fn_name, dtype, Qs, q_lengths, docs, doc_offsets, doc_lengths, scores=None):
+    _, d, stride, B = _marshal(Qs, docs, doc_offsets, doc_lengths, dtype)
+    ql = [int(x) for x in (q_lengths.tolist() if hasattr(q_lengths, "tolist") else q_lengths)]
+    nq = len(ql)
+    if sum(ql) != Qs.shape[0]:
+        raise ValueError("Qs must hold exactly the rows of the queries, back to back")
+    host = (ctypes.c_int32 * max(nq, 1))(*ql)
+    if scores is None:
+        scores = torch.empty((nq, B), dtype=torch.float32, device=docs.device)
+    elif scores.dtype != torch.float32 or tuple(scores.shape) != (nq, B) or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 [nq, B] tensor")
+    with torch.cuda.device(docs.device):
+        st = getattr(load(), fn_name)(
+            Qs.data_ptr(), ctypes.cast(host, ctypes.c_void_p), nq, d, docs.data_ptr(), stride,
+            doc_offsets.data_ptr(), doc_lengths.data_ptr(), B, scores.data_ptr(), _stream(docs),
+        )
+    _check(st, fn_name)
+    return scores
+
+
+def maxsim_rerank_multi(Qs, q_lengths, docs, doc_offsets, doc_lengths, scores=None) -> torch.Tensor:
+    """fp32 [nq, B] scores of nq queries (rows back to back in Qs, lengths q_lengths,
+    a host sequence) against the same B docs; fp16 inputs. Each doc tile is read once
+    per pass of up to 128 query rows (64 when d > 128)."""
+    return _rerank_multi("maxsim_rerank_multi", torch.float16, Qs, q_lengths, docs, doc_offsets,
+                         doc_lengths, scores)
+
+
+def maxsim_rerank_multi_bf16(Qs, q_lengths, docs, doc_offsets, doc_lengths, scores=None) -> torch.Tensor:
+    """maxsim_rerank_multi with bf16 inputs."""
+    return _rerank_multi("maxsim_rerank_multi_bf16", torch.bfloat16, Qs, q_lengths, docs, doc_offsets,
+                         doc_lengths, scores)
+
+
+def rerank_multi(Qs, q_lengths, docs, doc_offsets, doc_lengths, scores=None) -> torch.Tensor:
+    """maxsim_rerank_multi or maxsim_rerank_multi_bf16, chosen by Qs's dtype."""
+    fn = maxsim_rerank_multi_bf16 if Qs.dtype == torch.bfloat16 else maxsim_rerank_multi
+    return fn(Qs, q_lengths, docs, doc_offsets, doc_lengths, scores)

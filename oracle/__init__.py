@@ -25,6 +25,9 @@ tests/test_oracle_golden.py and tests/test_oracle_mutants.py):
   doc whose query index or rows are invalid scores NaN. Written as that selection plus
   ``maxsim``. Pinned by exact brute force per doc on tiny batches with interleaved,
   repeated, empty and invalid queries (tests/test_oracle_pairs.py).
+- ``maxsim_multi(...)``: several queries against the same docs, scores [nq, B]: the
+  single-query score per (query, doc). Pinned by exact brute force per (query, doc)
+  (tests/test_oracle_pairs.py).
 """
 
 from __future__ import annotations
@@ -36,8 +39,8 @@ import threading
 
 import numpy as np
 
-__all__ = ["FMT", "build", "Oracle", "decode", "maxsim", "maxsim_pairs", "maxsim_workload",
-           "max_threads"]
+__all__ = ["FMT", "build", "Oracle", "decode", "maxsim", "maxsim_pairs", "maxsim_multi",
+           "maxsim_workload", "max_threads"]
 
 FMT = {"f16": 0, "bf16": 1}
 
@@ -174,14 +177,30 @@ def maxsim_pairs(fmt, Qs, q_offsets, q_lengths, X, offsets, lengths, doc_query, 
     return out
 
 
+def maxsim_multi(fmt, Qs, q_lengths, X, offsets, lengths, d=None, threads: int = 0) -> np.ndarray:
+    """fp64 scores [nq, B]: query j (rows sum(q_lengths[:j]) .. + q_lengths[j] - 1 of
+    Qs) against every doc, as by ``maxsim``."""
+    Qs = np.ascontiguousarray(Qs, dtype=np.uint16)
+    q_lengths = np.asarray(q_lengths, np.int64)
+    out = np.empty((q_lengths.shape[0], np.asarray(offsets).shape[0]), np.float64)
+    lo = 0
+    for j, n in enumerate(q_lengths.tolist()):
+        out[j] = maxsim(fmt, Qs[lo:lo + n], X, offsets, lengths, d=d, threads=threads)
+        lo += n
+    return out
+
+
 def maxsim_workload(w, docs=None, threads: int = 0) -> np.ndarray:
-    """fp64 scores of a workloads.Workload, for all docs or for the doc ids `docs`."""
+    """fp64 scores of a workloads.Workload, for all docs or for the doc ids `docs`
+    ([nq, len(docs)] when several queries share the docs)."""
     offs, lens = w.offsets, w.lengths
     dq = w.doc_query
     if docs is not None:
         docs = np.asarray(docs, dtype=np.int64)
         offs, lens = offs[docs], lens[docs]
         dq = None if dq is None else dq[docs]
+    if w.q_lengths is not None and dq is None:
+        return maxsim_multi(w.dtype, w.Q, w.q_lengths, w.X, offs, lens, d=w.d, threads=threads)
     if dq is not None:
         return maxsim_pairs(w.dtype, w.Q, w.q_offsets, w.q_lengths, w.X, offs, lens, dq, w.Lq,
                             d=w.d, threads=threads)

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     for n in ("maxsim_rerank", "maxsim_rerank_bf16", "maxsim_status_string",
               "maxsim_workspace_size", "maxsim_plan", "maxsim_score", "maxsim_finish",
               "maxsim_version", "maxsim_rerank_pairs", "maxsim_rerank_pairs_bf16",
-              "maxsim_plan_pairs"):
+              "maxsim_plan_pairs", "maxsim_rerank_multi", "maxsim_rerank_multi_bf16"):
         assert n in names
 
 
@@ -165,3 +165,27 @@ def test_plan_pairs_validation(lib):
     assert plan(ws=None) == WORKSPACE
     assert plan(ws=FAKE + 128) == WORKSPACE
     assert plan(B=0, offs=None, lens=None, dq=None, ws=None) == OK
+
+
+@pytest.mark.parametrize("fn", ["maxsim_rerank_multi", "maxsim_rerank_multi_bf16"])
+def test_multi_host_validation(lib, fn):
+    ql = (ctypes.c_int32 * 3)(32, 0, 17)
+
+    def m(Qs=FAKE, q=ql, nq=3, d=128, docs=FAKE, stride=128, offs=FAKE, lens=FAKE + 1024, B=10,
+          scores=FAKE + 4096):
+        qp = ctypes.cast(q, ctypes.c_void_p) if q is not None else None
+        return getattr(lib, fn)(Qs, qp, nq, d, docs, stride, offs, lens, B, scores, None)
+
+    assert m(nq=-1) == INVALID
+    assert m(q=None) == INVALID
+    assert m(q=(ctypes.c_int32 * 3)(32, -1, 3)) == INVALID
+    assert m(q=(ctypes.c_int32 * 3)(32, 257, 3)) == UNSUPPORTED
+    assert m(Qs=None) == INVALID
+    assert m(Qs=FAKE + 8) == UNSUPPORTED
+    assert m(d=100, stride=104) == UNSUPPORTED
+    assert m(docs=None) == INVALID
+    assert m(scores=None) == INVALID
+    assert m(B=0) == OK
+    assert m(nq=0, q=None) == OK
+    assert m(nq=0, q=None, scores=None) == OK      # zero queries write nothing
+    assert m(Qs=None, q=(ctypes.c_int32 * 3)(0, 0, 0), B=0) == OK

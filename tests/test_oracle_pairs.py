@@ -1,4 +1,5 @@
-"""Pins of the oracle's multi-query ("pairs") form.
+"""Pins of the oracle's multi-query forms: "pairs" (each doc with its own query) and
+shared docs (every query against every doc).
 
 The Flash-MaxSim rerank page (docs.vllm.ai, vllm.v1.pool.flash_maxsim.
 flash_maxsim_rerank, kernel section `_maxsim_rerank_kernel`) names a pairs kernel without
@@ -121,3 +122,36 @@ def test_pairs_workload_shape():
     assert w.multi_query and w.nq == 3 and w.Lq == 32 and w.Q.shape == (68, 32)
     assert list(w.q_offsets) == [0, 16, 48]
     assert sorted(np.bincount(w.doc_query).tolist()) == [5, 7, 10]
+
+
+# ------------------------------------------------------------------ shared docs
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_multi_brute_force(fmt):
+    """Several queries against the same docs: scores[j, i] is query j's score of doc i."""
+    rng = np.random.default_rng([13, len(fmt)])
+    q_lengths = [2, 0, 4, 1]
+    lengths = rng.integers(0, 8, size=6)
+    lengths[0] = 0
+    w = workloads.custom_multi(q_lengths, 8, lengths, dtype=fmt, seed=17, order="shuffled", gap=(0, 2),
+                               stride=16)
+    got = oracle.maxsim_multi(fmt, w.Q, w.q_lengths, w.X, w.offsets, w.lengths, d=w.d)
+    assert got.shape == (4, 6)
+    lo = 0
+    for j, n in enumerate(q_lengths):
+        exact = brute_scores(fmt, w.Q[lo:lo + n], w.X, w.offsets, w.lengths, w.d)
+        _check(got[j], exact)
+        lo += n
+    assert np.all(got[1] == 0.0)  # the empty query
+
+
+def test_multi_matches_workload_and_rows_are_queries():
+    w = workloads.custom_multi([3, 5], 16, np.full(7, 4), seed=2)
+    assert w.shared_docs and not w.multi_query and w.nq == 2 and w.Q.shape == (8, 16)
+    got = oracle.maxsim_workload(w)
+    assert got.shape == (2, 7)
+    swapped = np.concatenate([w.Q[3:8], w.Q[0:3]])  # query 1 first, then query 0
+    w.Q, w.q_lengths = swapped, np.array([5, 3], np.int32)
+    got2 = oracle.maxsim_workload(w)
+    assert np.array_equal(got2[::-1], got)

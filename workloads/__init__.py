@@ -40,6 +40,8 @@ __all__ = [
     "large",
     "pairs",
     "custom_pairs",
+    "shared",
+    "custom_multi",
     "round_f16",
     "round_bf16",
     "F16_NAN",
@@ -70,8 +72,9 @@ class Workload:
     planted: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))
     notes: str = ""
     # Several queries in one batch (None: one query, Q itself). Query j is rows
-    # [q_offsets[j], q_offsets[j] + q_lengths[j]) of Q; doc i takes query doc_query[i];
-    # Lq is then the longest query.
+    # [q_offsets[j], q_offsets[j] + q_lengths[j]) of Q; Lq is then the longest query.
+    # With doc_query, doc i takes query doc_query[i] ("pairs"); without it, every
+    # query scores every doc (shared docs, scores [nq, B]).
     q_offsets: np.ndarray | None = None  # int32 [nq]
     q_lengths: np.ndarray | None = None  # int32 [nq]
     doc_query: np.ndarray | None = None  # int32 [B]
@@ -83,6 +86,10 @@ class Workload:
     @property
     def multi_query(self) -> bool:
         return self.doc_query is not None
+
+    @property
+    def shared_docs(self) -> bool:
+        return self.q_lengths is not None and self.doc_query is None
 
     @property
     def nq(self) -> int:
@@ -400,6 +407,31 @@ def pairs(seed: int = 5, **kw) -> Workload:
     return w
 
 
+def custom_multi(q_lengths, d: int, doc_lengths, *, dtype: str = "f16", seed: int = 0,
+                 name: str = "custom_multi", **kw) -> Workload:
+    """Several queries (rows back to back in Q, lengths q_lengths) that all score the
+    same docs. Other keywords go to custom() and shape the doc-row tensor."""
+    q_lengths = np.asarray(q_lengths, dtype=np.int64)
+    w = custom(0, d, doc_lengths, dtype=dtype, seed=seed, name=name, **kw)
+    rows = int(q_lengths.sum())
+    qrng = np.random.default_rng([seed, _S_Q])
+    w.Q = _round(_unit_rows(qrng, rows, d), dtype) if rows else np.zeros((0, d), np.uint16)
+    w.Lq = int(q_lengths.max()) if q_lengths.size else 0
+    q_offsets = np.concatenate([[0], np.cumsum(q_lengths)[:-1]]) if q_lengths.size else q_lengths
+    w.q_offsets = q_offsets.astype(np.int32)
+    w.q_lengths = q_lengths.astype(np.int32)
+    return w
+
+
+def shared(seed: int = 6, **kw) -> Workload:
+    """8 queries of 32 rows against the same 80,000 fp16 docs of U[64,448] rows, d 128,
+    packed back to back in doc order (~20.5 M rows, 5.2 GB): e.g. query variants or
+    several users over one candidate set."""
+    meta = np.random.default_rng([seed, _S_META, 0])
+    lengths = meta.integers(64, 448, size=80_000, endpoint=True)
+    return custom_multi(np.full(8, 32), 128, lengths, dtype="f16", seed=seed, name="shared", **kw)
+
+
 CONFIGS = {
     "tiny": tiny,
     "colbert": colbert,
@@ -407,6 +439,7 @@ CONFIGS = {
     "scattered": scattered,
     "large": large,
     "pairs": pairs,
+    "shared": shared,
 }
 
 
