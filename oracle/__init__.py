@@ -28,6 +28,12 @@ tests/test_oracle_golden.py and tests/test_oracle_mutants.py):
 - ``maxsim_multi(...)``: several queries against the same docs, scores [nq, B]: the
   single-query score per (query, doc). Pinned by exact brute force per (query, doc)
   (tests/test_oracle_pairs.py).
+- ``decode_e4m3(bits)`` and ``maxsim_fp8(...)``: docs stored as FP8 E4M3 bits with one
+  fp32 scale for the doc tensor (element = scale * e4m3), the query fp16 or bf16, as
+  FP8 caches are dequantised with a per-tensor scale on the sparse prefill pages page
+  (`stage_prefill_pages`). The decoder is pinned on all 256 patterns against torch's
+  float8_e4m3fn; the score by exact brute force, one-hot closed forms and the
+  equality with ``maxsim`` on the decoded values (tests/test_oracle_fp8.py).
 """
 
 from __future__ import annotations
@@ -39,8 +45,8 @@ import threading
 
 import numpy as np
 
-__all__ = ["FMT", "build", "Oracle", "decode", "maxsim", "maxsim_pairs", "maxsim_multi",
-           "maxsim_workload", "max_threads"]
+__all__ = ["FMT", "build", "Oracle", "decode", "decode_e4m3", "maxsim", "maxsim_fp8",
+           "maxsim_pairs", "maxsim_multi", "maxsim_workload", "max_threads"]
 
 FMT = {"f16": 0, "bf16": 1}
 
@@ -90,6 +96,14 @@ class Oracle:
             ctypes.c_int32, ctypes.c_void_p, ctypes.c_int,
         ]
         lib.oracle_max_threads.restype = ctypes.c_int
+        lib.oracle_decode_e4m3_table.restype = None
+        lib.oracle_decode_e4m3_table.argtypes = [ctypes.c_void_p]
+        lib.maxsim_oracle_fp8_f64.restype = ctypes.c_int
+        lib.maxsim_oracle_fp8_f64.argtypes = [
+            ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+            ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p,
+            ctypes.c_int32, ctypes.c_double, ctypes.c_void_p, ctypes.c_int,
+        ]
         self.lib = lib
         self.path = path
 
@@ -130,6 +144,35 @@ class Oracle:
             raise ValueError(f"maxsim_oracle_f64 failed ({rc})")
         return out
 
+    def decode_e4m3(self, bits: np.ndarray) -> np.ndarray:
+        table = np.empty(256, np.float64)
+        self.lib.oracle_decode_e4m3_table(table.ctypes.data)
+        return table[np.asarray(bits, dtype=np.uint8)]
+
+    def maxsim_fp8(self, qfmt: str, Q: np.ndarray, X8: np.ndarray, offsets, lengths, doc_scale: float,
+                   d: int | None = None, threads: int = 0) -> np.ndarray:
+        """fp64 scores: Q uint16 [Lq, d] bits (fp16 or bf16), X8 uint8 [T, stride] E4M3
+        bits, doc element = doc_scale * e4m3."""
+        Q = np.ascontiguousarray(Q, dtype=np.uint16)
+        X8 = np.ascontiguousarray(X8, dtype=np.uint8)
+        if Q.ndim != 2 or X8.ndim != 2:
+            raise ValueError("Q and X8 must be 2-D")
+        Lq = Q.shape[0]
+        d = Q.shape[1] if d is None else int(d)
+        offs = np.ascontiguousarray(offsets, dtype=np.int32)
+        lens = np.ascontiguousarray(lengths, dtype=np.int32)
+        B = offs.shape[0]
+        out = np.empty(B, np.float64)
+        if B == 0:
+            return out
+        rc = self.lib.maxsim_oracle_fp8_f64(
+            FMT[qfmt], Q.ctypes.data, Lq, d, X8.ctypes.data, X8.shape[1], offs.ctypes.data,
+            lens.ctypes.data, B, float(doc_scale), out.ctypes.data, int(threads),
+        )
+        if rc:
+            raise ValueError(f"maxsim_oracle_fp8_f64 failed ({rc})")
+        return out
+
 
 def _get() -> Oracle:
     global _default
@@ -146,6 +189,15 @@ def decode(bits: np.ndarray, fmt: str) -> np.ndarray:
 
 def maxsim(fmt, Q, X, offsets, lengths, d=None, threads: int = 0) -> np.ndarray:
     return _get().maxsim(fmt, Q, X, offsets, lengths, d=d, threads=threads)
+
+
+def decode_e4m3(bits: np.ndarray) -> np.ndarray:
+    """The oracle's decoding of FP8 E4M3 bytes to float64."""
+    return _get().decode_e4m3(bits)
+
+
+def maxsim_fp8(qfmt, Q, X8, offsets, lengths, doc_scale, d=None, threads: int = 0) -> np.ndarray:
+    return _get().maxsim_fp8(qfmt, Q, X8, offsets, lengths, doc_scale, d=d, threads=threads)
 
 
 def maxsim_pairs(fmt, Qs, q_offsets, q_lengths, X, offsets, lengths, doc_query, max_lq,
@@ -199,6 +251,8 @@ def maxsim_workload(w, docs=None, threads: int = 0) -> np.ndarray:
         docs = np.asarray(docs, dtype=np.int64)
         offs, lens = offs[docs], lens[docs]
         dq = None if dq is None else dq[docs]
+    if w.X8 is not None:
+        return maxsim_fp8(w.dtype, w.Q, w.X8, offs, lens, w.doc_scale, d=w.d, threads=threads)
     if w.q_lengths is not None and dq is None:
         return maxsim_multi(w.dtype, w.Q, w.q_lengths, w.X, offs, lens, d=w.d, threads=threads)
     if dq is not None:

@@ -162,6 +162,99 @@ int maxsim_oracle_f64(int fmt, const uint16_t *Q, int32_t Lq, int32_t d,
     return 0;
 }
 
+/*
+ * FP8 E4M3 ("e4m3fn" of the OCP 8-bit floating point formats): 1 sign bit, 4 exponent
+ * bits (bias 7), 3 fraction bits, no infinities.
+ *   exponent 0                   -> subnormal (or zero):  fraction * 2^-9
+ *   exponent 1..15 (not S.1111.111) -> normal: (8 + fraction) * 2^(exponent - 10)
+ *   S.1111.111                   -> NaN
+ * Largest finite magnitude 448 (S.1111.110).
+ */
+double oracle_decode_e4m3(uint8_t b)
+{
+    int sign = (b >> 7) & 1;
+    int expo = (b >> 3) & 0xF;
+    int frac = b & 0x7;
+    double v;
+    if (expo == 15 && frac == 7)
+        return NAN;
+    if (expo == 0)
+        v = ldexp((double)frac, -9);
+    else
+        v = ldexp((double)(8 + frac), expo - 10);
+    return sign ? -v : v;
+}
+
+/* Decoded value of every 8-bit E4M3 pattern (out has 256 entries). */
+void oracle_decode_e4m3_table(double *out)
+{
+    for (uint32_t u = 0; u < 256u; ++u)
+        out[u] = oracle_decode_e4m3((uint8_t)u);
+}
+
+/*
+ * Docs stored as FP8 E4M3 bits with one scale for the whole doc tensor: doc element
+ * = doc_scale * e4m3(bits), as FP8 caches are dequantised with a per-tensor scale
+ * (sparse prefill pages page, docs.vllm.ai, `stage_prefill_pages`: FP8 E4M3 pages
+ * with k/v scales). The query stays fp16 or bf16 (qfmt). Same definition and loop
+ * order as maxsim_oracle_f64.
+ *
+ * X  raw bytes, doc row t of doc i at X + (offsets[i] + t) * stride (stride in
+ *    elements = bytes)
+ */
+int maxsim_oracle_fp8_f64(int qfmt, const uint16_t *Q, int32_t Lq, int32_t d,
+                          const uint8_t *X, int64_t stride,
+                          const int32_t *offsets, const int32_t *lengths, int32_t B,
+                          double doc_scale, double *scores, int nthreads)
+{
+    if (qfmt != ORACLE_FMT_F16 && qfmt != ORACLE_FMT_BF16)
+        return 1;
+    if (Lq < 0 || d < 0 || B < 0 || stride < d)
+        return 1;
+
+    double *tab = (double *)malloc(65536 * sizeof(double));
+    double *Qd = (double *)malloc(((size_t)Lq * (size_t)d + 1) * sizeof(double));
+    if (!tab || !Qd) {
+        free(tab);
+        free(Qd);
+        return 1;
+    }
+    oracle_decode_table(qfmt, tab);
+    for (int64_t e = 0; e < (int64_t)Lq * d; ++e)
+        Qd[e] = tab[Q[e]];
+    double xtab[256];
+    for (uint32_t u = 0; u < 256u; ++u)
+        xtab[u] = doc_scale * oracle_decode_e4m3((uint8_t)u);
+
+#ifdef _OPENMP
+    if (nthreads <= 0)
+        nthreads = omp_get_max_threads();
+#pragma omp parallel for schedule(dynamic, 1) num_threads(nthreads)
+#endif
+    for (int32_t i = 0; i < B; ++i) {
+        const int64_t off = (int64_t)offsets[i];
+        const int64_t len = (int64_t)lengths[i];
+        double s = 0.0;
+        for (int32_t q = 0; q < Lq; ++q) {
+            double m = -INFINITY;
+            for (int64_t t = 0; t < len; ++t) {
+                const uint8_t *row = X + (off + t) * stride;
+                double dot = 0.0;
+                for (int32_t k = 0; k < d; ++k)
+                    dot += Qd[(int64_t)q * d + k] * xtab[row[k]];
+                if (dot > m)
+                    m = dot;
+            }
+            s += m;
+        }
+        scores[i] = s;
+    }
+
+    free(tab);
+    free(Qd);
+    return 0;
+}
+
 /* Threads an OpenMP parallel region of this library would use by default. */
 int oracle_max_threads(void)
 {

@@ -122,8 +122,73 @@ def pin_int64_addressing(o):
     assert np.array_equal(got, ref), (got, ref)
 
 
+def _e4m3_vals(bits):
+    """float64 of FP8 E4M3 bytes by torch's float8_e4m3fn (not the oracle's decoder)."""
+    import torch
+
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).view(torch.float8_e4m3fn)
+    return t.to(torch.float64).numpy()
+
+
+def pin_e4m3_decoder(o):
+    bits = np.arange(256, dtype=np.uint8)
+    got = o.decode_e4m3(bits)
+    ref = _e4m3_vals(bits)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def _fp8_case(fmt, Lq, d, lengths, seed, scale, all_patterns=False):
+    w = workloads.custom(Lq, d, lengths, dtype=fmt, seed=seed, order="shuffled", gap=(0, 3),
+                         gap_fill="nan")
+    workloads.to_fp8(w, doc_scale=scale, stride8=d + 5)
+    if all_patterns:  # every finite byte somewhere in the docs
+        rng = np.random.default_rng(seed)
+        finite = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+        for o_, n in zip(w.offsets, w.lengths):
+            w.X8[o_:o_ + n, :d] = rng.choice(finite, size=(n, d))
+    return w
+
+
+def pin_fp8_brute_force(o):
+    from fractions import Fraction
+
+    for fmt in ("f16", "bf16"):
+        for scale in (1.0, 0.37, 2.0 ** -7):
+            w = _fp8_case(fmt, 3, 8, [0, 4, 1, 6, 3], seed=int(scale * 100) + len(fmt), scale=scale,
+                          all_patterns=True)
+            Qv = _vals(w.Q, fmt)
+            Xv = _e4m3_vals(w.X8)
+            sc = Fraction(float(np.float32(scale)))
+            got = o.maxsim_fp8(fmt, w.Q, w.X8, w.offsets, w.lengths, w.doc_scale, d=w.d)
+            for i, (a, n) in enumerate(zip(w.offsets, w.lengths)):
+                if n == 0:
+                    assert got[i] == float("-inf")
+                    continue
+                tot = Fraction(0)
+                for q in range(w.Lq):
+                    tot += max(sum(Fraction(float(Qv[q, k])) * sc * Fraction(float(Xv[a + t, k]))
+                                   for k in range(w.d)) for t in range(n))
+                assert abs(got[i] - float(tot)) <= 1e-12 * (1 + abs(float(tot))), (fmt, scale, i)
+
+
+def pin_fp8_equals_f16_path(o):
+    """With a power-of-two scale every doc value is exact in fp16: the FP8 score equals
+    the fp16 oracle on those values, bit for bit (same loop order)."""
+    w = _fp8_case("f16", 5, 24, [3, 0, 7, 1, 9], seed=21, scale=2.0 ** -6, all_patterns=True)
+    vals = _e4m3_vals(w.X8[:, : w.d]) * w.doc_scale
+    vals[np.isnan(vals)] = 0.0
+    X16 = np.ascontiguousarray(vals.astype(np.float16)).view(np.uint16)
+    assert np.array_equal(X16.view(np.float16).astype(np.float64), vals)
+    got = o.maxsim_fp8("f16", w.Q, w.X8, w.offsets, w.lengths, w.doc_scale, d=w.d)
+    ref = o.maxsim("f16", w.Q, X16, w.offsets, w.lengths, d=w.d)
+    assert np.array_equal(got, ref)
+
+
 PINS = [pin_decoders, pin_brute_force, pin_golden, pin_closed_forms, pin_one_hot,
-        pin_int64_addressing]
+        pin_int64_addressing, pin_e4m3_decoder, pin_fp8_brute_force, pin_fp8_equals_f16_path]
 
 
 def run(o) -> list[str]:

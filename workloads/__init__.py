@@ -42,6 +42,9 @@ __all__ = [
     "custom_pairs",
     "shared",
     "custom_multi",
+    "large_fp8",
+    "to_fp8",
+    "E4M3_NAN",
     "round_f16",
     "round_bf16",
     "F16_NAN",
@@ -50,6 +53,7 @@ __all__ = [
 
 F16_NAN = 0x7E00
 BF16_NAN = 0x7FC0
+E4M3_NAN = 0x7F
 _CHUNK_ROWS = 1 << 18
 
 _S_META, _S_Q, _S_ROWS, _S_PLANT = 0, 1, 2, 3
@@ -78,6 +82,9 @@ class Workload:
     q_offsets: np.ndarray | None = None  # int32 [nq]
     q_lengths: np.ndarray | None = None  # int32 [nq]
     doc_query: np.ndarray | None = None  # int32 [B]
+    # Docs stored as FP8 E4M3 bits (None: X holds them): element = doc_scale * e4m3.
+    X8: np.ndarray | None = None         # uint8 [T, stride8]
+    doc_scale: float = 1.0
 
     @property
     def B(self) -> int:
@@ -97,7 +104,7 @@ class Workload:
 
     @property
     def T(self) -> int:
-        return int(self.X.shape[0])
+        return int((self.X8 if self.X8 is not None else self.X).shape[0])
 
     @property
     def doc_tokens(self) -> int:
@@ -105,8 +112,8 @@ class Workload:
 
     @property
     def doc_bytes(self) -> int:
-        """Bytes of doc rows the method must read: 2*d per doc token."""
-        return self.doc_tokens * 2 * self.d
+        """Bytes of doc rows the method must read: 2*d per doc token (d with FP8 docs)."""
+        return self.doc_tokens * (1 if self.X8 is not None else 2) * self.d
 
 
 # --------------------------------------------------------------------------- rounding
@@ -407,6 +414,40 @@ def pairs(seed: int = 5, **kw) -> Workload:
     return w
 
 
+def to_fp8(w: Workload, doc_scale: float = 2.0 ** -8, stride8: int | None = None,
+           keep_x: bool = True) -> Workload:
+    """Store w's docs as FP8 E4M3: X8 = e4m3(decode(X) / doc_scale), round to nearest
+    even by torch's float8_e4m3fn conversion (no value reaches 448 for unit rows at
+    the default scale). Rows are stride8 bytes apart (default: the row width rounded
+    up to 16); bytes past d hold the E4M3 NaN pattern, as do rows that held NaN.
+    The scale is stored rounded to fp32."""
+    import torch
+
+    d = w.d
+    stride8 = ((d + 15) // 16) * 16 if stride8 is None else int(stride8)
+    if stride8 < d:
+        raise ValueError("stride8 must be >= d")
+    doc_scale = float(np.float32(doc_scale))
+    X8 = np.full((w.T, stride8), E4M3_NAN, np.uint8)
+    for r0 in range(0, w.T, _CHUNK_ROWS):
+        r1 = min(w.T, r0 + _CHUNK_ROWS)
+        v = _bits_to_f32(np.ascontiguousarray(w.X[r0:r1, :d]), w.dtype) / np.float32(doc_scale)
+        X8[r0:r1, :d] = torch.from_numpy(v).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    w.X8 = X8
+    w.doc_scale = doc_scale
+    if not keep_x:
+        w.X = np.zeros((0, w.stride), np.uint16)
+    return w
+
+
+def large_fp8(seed: int = 4, **kw) -> Workload:
+    """The large workload (same docs, query and seed) with docs stored as FP8 E4M3,
+    doc scale 2^-8, rows 128 bytes apart (~2.6 GB)."""
+    w = large(seed=seed, **kw)
+    w.name = "large_fp8"
+    return to_fp8(w, keep_x=False)
+
+
 def custom_multi(q_lengths, d: int, doc_lengths, *, dtype: str = "f16", seed: int = 0,
                  name: str = "custom_multi", **kw) -> Workload:
     """Several queries (rows back to back in Q, lengths q_lengths) that all score the
@@ -440,6 +481,7 @@ CONFIGS = {
     "large": large,
     "pairs": pairs,
     "shared": shared,
+    "large_fp8": large_fp8,
 }
 
 
