@@ -15,7 +15,8 @@ holding a planted near-duplicate of a query row.
 --workload shared times 8 queries of 32 rows against the same 80,000 docs
 (maxsim_rerank_multi, one call: plan, then per pass of 128 query rows a score and a
 combine launch); its events bracket the whole call, and a doc token counts once per
-query that scores it.
+query that scores it. --workload large_fp8 times the large workload with docs stored as
+FP8 E4M3 bytes (scale 2^-8; maxsim_plan, maxsim_score_fp8, maxsim_finish_fp8).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload large]
                     [--no-cpu-baseline] [--copy-probe]
@@ -71,15 +72,16 @@ def measured_traffic(workload: str):
 
 
 def algorithmic_bytes(w) -> int:
-    """Doc rows read once (2 d bytes per doc token), 8 B of offset/length and 4 B of
+    """Doc rows read once (2 d bytes per doc token, d with FP8 docs), 8 B of offset/length and 4 B of
     score per doc, and the query rows once; a multi-query batch adds each doc's 4 B
     query index and 8 B of offset/length per query; queries sharing the docs write
     4 B of score per (query, doc)."""
     q_bytes = w.Q.shape[0] * w.d * 2
     if w.shared_docs:
-        return w.doc_tokens * 2 * w.d + w.B * (8 + 4 * w.nq) + q_bytes
-        return w.doc_tokens * 2 * w.d + w.B * 16 + q_bytes + w.nq * 8
-    return w.doc_tokens * 2 * w.d + w.B * 12 + q_bytes
+        return w.doc_bytes + w.B * (8 + 4 * w.nq) + q_bytes
+    if w.multi_query:
+        return w.doc_bytes + w.B * 16 + q_bytes + w.nq * 8
+    return w.doc_bytes + w.B * 12 + q_bytes
 
 
 def algorithmic_flops(w) -> float:
@@ -202,7 +204,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large",
-                    choices=["tiny", "colbert", "long_doc", "scattered", "large", "pairs", "shared"])
+                    choices=["tiny", "colbert", "long_doc", "scattered", "large", "pairs", "shared",
+                             "large_fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one plain 2 GiB device copy (counter calibration)")
@@ -232,7 +235,10 @@ def main() -> int:
     log(f"generated B={w.B} rows={w.T} doc tokens={w.doc_tokens} in {time.perf_counter() - t0:.1f} s")
     tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
     Q = torch.from_numpy(w.Q.view(np.int16)).to(dev).view(tdt)
-    X = torch.from_numpy(w.X.view(np.int16)).to(dev).view(tdt)[:, : w.d]
+    if w.X8 is not None:
+        X = torch.from_numpy(w.X8).to(dev)[:, : w.d]
+    else:
+        X = torch.from_numpy(w.X.view(np.int16)).to(dev).view(tdt)[:, : w.d]
     offs = torch.from_numpy(w.offsets).to(dev)
     lens = torch.from_numpy(w.lengths).to(dev)
     scores = torch.empty(w.B, dtype=torch.float32, device=dev)
@@ -265,10 +271,16 @@ def main() -> int:
         plan()
         if ev_a is not None:
             ev_a.record()
-        lir.maxsim_score(Q, X, offs, lens, ws, scores=scores, Lq=w.Lq)
+        if w.X8 is not None:
+            lir.maxsim_score_fp8(Q, X, offs, lens, w.doc_scale, ws, scores=scores)
+        else:
+            lir.maxsim_score(Q, X, offs, lens, ws, scores=scores, Lq=w.Lq)
         if ev_b is not None:
             ev_b.record()
-        lir.maxsim_finish(Q, w.B, ws, scores, Lq=w.Lq)
+        if w.X8 is not None:
+            lir.maxsim_finish_fp8(Q, w.B, w.doc_scale, ws, scores)
+        else:
+            lir.maxsim_finish(Q, w.B, ws, scores, Lq=w.Lq)
 
     for _ in range(args.warmup):
         step()
@@ -317,12 +329,14 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16" if w.dtype == "f16" else "bf16",
+        "dtype": ("fp8e4m3 docs, " if w.X8 is not None else "") + ("f16" if w.dtype == "f16" else "bf16"),
         "data": "synthetic",
         "config": {
             "workload": f"{w.name}: " + (f"{w.nq} queries of up to " if w.multi_query else "")
                         + f"Lq={w.Lq} d={w.d} B={w.B} {w.dtype}, "
-                        f"{w.doc_tokens} doc tokens in a [{w.T}, {w.stride}] tensor, seed {w.seed}",
+                        f"{w.doc_tokens} doc tokens in a [{w.T}, {w.X8.shape[1] if w.X8 is not None else w.stride}] "
+                        + ("FP8 E4M3 (scale %g) " % w.doc_scale if w.X8 is not None else "")
+                        + f"tensor, seed {w.seed}",
             "Lq": w.Lq, "d": w.d, "B": w.B, "doc_tokens": w.doc_tokens, "rows": w.T,
             "queries": w.nq,
             "parallelism": "1 GPU",

@@ -153,6 +153,33 @@ MAXSIM_API int maxsim_rerank_multi_bf16(const void *Qs, const int32_t *q_lengths
                              const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
                              float *scores, void *stream);
 
+/*
+ * Docs stored as FP8 E4M3 ("e4m3fn": 4 exponent bits, bias 7, 3 fraction bits,
+ * largest finite 448, S.1111.111 = NaN) with one fp32 scale for the whole doc tensor:
+ * doc element = doc_scale * e4m3(byte). Half the bytes of fp16 docs on a path bound by
+ * reading them. FP8 caches dequantised with per-tensor scales are the sparse prefill
+ * pages page's (docs.vllm.ai, `stage_prefill_pages`: FP8 E4M3 pages with k/v scales).
+ * The query stays fp16 (maxsim_rerank_fp8) or bf16 (maxsim_rerank_fp8_bf16); each doc
+ * value is converted exactly to the query's format, products and sums are fp32 as in
+ * maxsim_rerank, and the sum is multiplied by doc_scale.
+ *
+ * docs:      FP8 E4M3 bytes, row r at docs + r * stride (stride in bytes = elements),
+ *            16-byte aligned.
+ * doc_scale: finite, > 0 (MAXSIM_ERR_INVALID_ARG otherwise).
+ * Envelope: d % 16 == 0 and stride % 16 == 0 (MAXSIM_ERR_UNSUPPORTED otherwise), the
+ * rest as for maxsim_rerank. Quantising docs to E4M3 is the caller's step.
+ */
+MAXSIM_API int maxsim_rerank_fp8(const void *Q, int32_t Lq, int32_t d,
+                      const void *docs, int64_t stride,
+                      const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                      float doc_scale, float *scores, void *stream);
+
+/* Same as maxsim_rerank_fp8 with a bf16 query. */
+MAXSIM_API int maxsim_rerank_fp8_bf16(const void *Q, int32_t Lq, int32_t d,
+                           const void *docs, int64_t stride,
+                           const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                           float doc_scale, float *scores, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 MAXSIM_API const char *maxsim_status_string(int status);
 
@@ -207,6 +234,20 @@ MAXSIM_API int maxsim_score(int dtype, const void *Q, int32_t Lq, int32_t d,
 
 MAXSIM_API int maxsim_finish(int dtype, int32_t Lq, int32_t d, int32_t B, float *scores,
                   void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Staged score and finish for FP8 E4M3 docs (maxsim_rerank_fp8's operation; dtype is
+ * the query's format, MAXSIM_F16 or MAXSIM_BF16). The plan and the workspace are the
+ * same as above (maxsim_plan, maxsim_workspace_size).
+ */
+MAXSIM_API int maxsim_score_fp8(int dtype, const void *Q, int32_t Lq, int32_t d,
+                     const void *docs, int64_t stride,
+                     const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                     float doc_scale, float *scores,
+                     void *workspace, size_t workspace_bytes, void *stream);
+
+MAXSIM_API int maxsim_finish_fp8(int dtype, int32_t Lq, int32_t d, int32_t B, float doc_scale,
+                      float *scores, void *workspace, size_t workspace_bytes, void *stream);
 
 /* Library version as major*10000 + minor*100 + patch. */
 MAXSIM_API int maxsim_version(void);

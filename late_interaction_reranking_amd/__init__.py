@@ -6,7 +6,8 @@ score_i = sum over query rows of the best dot product with any of document i's r
 (Flash-MaxSim rerank page, docs.vllm.ai, vllm.v1.pool.flash_maxsim.flash_maxsim_rerank).
 The pairs entry points score a batch of many queries in one launch, each document
 against its own query; the multi entry points score several queries against the same
-documents, reading each document tile once for a pass of up to 128 query rows.
+documents, reading each document tile once for a pass of up to 128 query rows; the
+fp8 entry points read documents stored as FP8 E4M3 bytes with one scale.
 
 The computation lives in libmaxsim.so (hand-written HIP, C ABI in include/maxsim.h);
 this package is its ctypes binding. Build the library with
@@ -28,7 +29,10 @@ from .maxsim import (  # noqa: F401
     maxsim_rerank_pairs,
     maxsim_rerank_pairs_bf16,
     maxsim_finish,
+    maxsim_finish_fp8,
+    maxsim_rerank_fp8,
     maxsim_score,
+    maxsim_score_fp8,
     maxsim_status_string,
     maxsim_version,
     maxsim_workspace_size,

@@ -115,6 +115,7 @@ struct ScoreArgs {
     float *scores;
     int32_t d, ngroups, lq_pad;
     int32_t q_in_lds;         // LDS holds room for the Q tile; used unless the plan is multi-query
+    float doc_scale;          // FP8 docs: value = doc_scale * e4m3 (unused otherwise)
     QueryTiles qt;
 };
 
@@ -131,6 +132,7 @@ struct CombineArgs {
     float *scores;
     uint32_t score_waves;     // W of the score launch (fixes the chunking)
     int32_t nqt, ngroups, lq_pad;
+    float doc_scale;          // multiplies each sum (1 for 16-bit docs)
     QueryTiles qt;            // as in ScoreArgs
 };
 

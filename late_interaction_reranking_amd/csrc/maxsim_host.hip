@@ -36,6 +36,8 @@ using namespace maxsim;
     }
 MAXSIM_DECLARE_LOOKUPS(f16)
 MAXSIM_DECLARE_LOOKUPS(bf16)
+MAXSIM_DECLARE_LOOKUPS(f16_fp8)
+MAXSIM_DECLARE_LOOKUPS(bf16_fp8)
 #undef MAXSIM_DECLARE_LOOKUPS
 
 namespace {
@@ -291,8 +293,8 @@ combine_kernel(const CombineArgs a)
                     const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
                     // NaN for an invalid query, chosen and stored as bits (the
                     // library is compiled without NaN semantics for its max steps).
-                    const uint32_t v = pairs && q_len < 0 ? kNaNBits
-                                                          : __builtin_bit_cast(uint32_t, ((s0 + s1) + s2) + s3);
+                    const float sum = (((s0 + s1) + s2) + s3) * a.doc_scale;
+                    const uint32_t v = pairs && q_len < 0 ? kNaNBits : __builtin_bit_cast(uint32_t, sum);
                     if (lane == 0) reinterpret_cast<uint32_t *>(a.scores)[(size_t)end * a.qt.score_stride + doc] = v;
                     lane_sum = 0.0f;
                 }
@@ -412,9 +414,24 @@ bool q_staged(const Config &c) { return q_lds_bytes(c) <= kMaxQLdsBytes; }
 // Dynamic LDS of the score kernel: the Q tile (if it fits), then one staging tile per
 // wave, 16 rows of (d/8 | 1) 16-byte chunks, plus one slot that lanes with nothing to
 // stage write.
-size_t score_lds_bytes(const Config &c, int32_t d)
+// Kernel formats: bit 0 = bf16 query (MAXSIM_BF16), bit 1 = docs stored as FP8 E4M3.
+constexpr int kFmtFp8Docs = 2;
+
+size_t score_lds_bytes(const Config &c, int32_t d, int fmt)
 {
-    return (q_staged(c) ? q_lds_bytes(c) : 0) + (size_t)kScoreWaves * (kTileRows * ((d / 8) | 1) + 1) * 16;
+    const int chunks = (fmt & kFmtFp8Docs) ? d / 16 : d / 8;
+    return (q_staged(c) ? q_lds_bytes(c) : 0) + (size_t)kScoreWaves * (kTileRows * (chunks | 1) + 1) * 16;
+}
+
+const void *score_fn(int fmt, const Config &c)
+{
+    switch (fmt) {
+    case MAXSIM_F16: return maxsim_score_kernel_f16(c.nks, c.nqt);
+    case MAXSIM_BF16: return maxsim_score_kernel_bf16(c.nks, c.nqt);
+    case MAXSIM_F16 | kFmtFp8Docs: return maxsim_score_kernel_f16_fp8(c.nks, c.nqt);
+    case MAXSIM_BF16 | kFmtFp8Docs: return maxsim_score_kernel_bf16_fp8(c.nks, c.nqt);
+    default: return nullptr;
+    }
 }
 
 // scores_needed = false: no score is written (zero queries), so scores may be null.
@@ -500,16 +517,17 @@ QueryTiles single_tiles(int32_t Lq)
 
 // Lq: rows of the one query, the longest query of a pairs plan, or 16 x the query
 // tiles of a launch over several queries sharing the docs (qt describes them).
-int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
-                 float *scores, const Layout &L, char *ws, const QueryTiles &qt, hipStream_t stream)
+// fmt: kernel format (query format | kFmtFp8Docs); doc_scale multiplies FP8 doc sums.
+int launch_score(int fmt, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                 float *scores, const Layout &L, char *ws, const QueryTiles &qt, float doc_scale,
+                 hipStream_t stream)
 {
     const Config c = choose_config(Lq, d);
     if (c.lq_pad > kMaxLqPad || c.nqt * c.nks > kMaxFragsPerGroup) return MAXSIM_ERR_UNSUPPORTED;
-    const void *fn = dtype == MAXSIM_BF16 ? maxsim_score_kernel_bf16(c.nks, c.nqt)
-                                          : maxsim_score_kernel_f16(c.nks, c.nqt);
+    const void *fn = score_fn(fmt, c);
     if (!fn) return MAXSIM_ERR_UNSUPPORTED;
     const bool q_in_lds = q_staged(c);
-    const size_t lds = score_lds_bytes(c, d);
+    const size_t lds = score_lds_bytes(c, d, fmt);
     int per_cu = 0;
     if (score_blocks_per_cu(fn, lds, &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     DeviceFacts f;
@@ -517,7 +535,7 @@ int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     ScoreArgs a;
     a.Q = static_cast<const uint16_t *>(Q);
     a.docs = static_cast<const char *>(docs);
-    a.stride_bytes = stride * 2;
+    a.stride_bytes = stride * ((fmt & kFmtFp8Docs) ? 1 : 2);
     a.hdr = reinterpret_cast<const Header *>(ws + L.header);
     a.desc = reinterpret_cast<const DocDesc *>(ws + L.desc);
     a.partials = reinterpret_cast<float *>(ws + L.partials);
@@ -527,6 +545,7 @@ int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     a.lq_pad = c.lq_pad;
     a.q_in_lds = q_in_lds ? 1 : 0;
     a.qt = qt;
+    a.doc_scale = doc_scale;
     void *args[] = {&a};
     const dim3 grid((unsigned)(f.cus * per_cu));
     if (hipLaunchKernel(fn, grid, dim3(kScoreBlock), args, lds, stream) != hipSuccess) return MAXSIM_ERR_HIP;
@@ -535,16 +554,15 @@ int launch_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
 
 // The combine kernel recomputes the score kernel's chunking, which depends on that
 // launch's wave count: the same instance and occupancy are looked up here.
-int launch_finish(int dtype, int32_t Lq, int32_t d, float *scores, const Layout &L, char *ws,
-                  const QueryTiles &qt, hipStream_t stream)
+int launch_finish(int fmt, int32_t Lq, int32_t d, float *scores, const Layout &L, char *ws,
+                  const QueryTiles &qt, float doc_scale, hipStream_t stream)
 {
     const Config c = choose_config(Lq, d);
     if (c.lq_pad > kMaxLqPad || c.nqt * c.nks > kMaxFragsPerGroup) return MAXSIM_ERR_UNSUPPORTED;
-    const void *fn = dtype == MAXSIM_BF16 ? maxsim_score_kernel_bf16(c.nks, c.nqt)
-                                          : maxsim_score_kernel_f16(c.nks, c.nqt);
+    const void *fn = score_fn(fmt, c);
     if (!fn) return MAXSIM_ERR_UNSUPPORTED;
     int per_cu = 0;
-    if (score_blocks_per_cu(fn, score_lds_bytes(c, d), &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    if (score_blocks_per_cu(fn, score_lds_bytes(c, d, fmt), &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     DeviceFacts f;
     if (current_facts(&f) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     CombineArgs ca;
@@ -557,15 +575,16 @@ int launch_finish(int dtype, int32_t Lq, int32_t d, float *scores, const Layout 
     ca.ngroups = c.ngroups;
     ca.lq_pad = c.lq_pad;
     ca.qt = qt;
+    ca.doc_scale = (fmt & kFmtFp8Docs) ? doc_scale : 1.0f;
     hipLaunchKernelGGL(combine_kernel, dim3((unsigned)f.cus * 4u), dim3(kScoreBlock), 0, stream, ca);
     return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
 }
 
 // Plan, score and combine with a stream-ordered temporary workspace; qt.max_lq sizes
 // the kernel configuration.
-int run_all(int dtype, const void *Q, const QueryTable &qt, int32_t d, const void *docs,
+int run_all(int fmt, const void *Q, const QueryTable &qt, int32_t d, const void *docs,
             int64_t stride, const int32_t *offsets, const int32_t *lengths, int32_t B, float *scores,
-            hipStream_t stream)
+            float doc_scale, hipStream_t stream)
 {
     Layout L;
     if (workspace_layout(qt.max_lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
@@ -574,8 +593,9 @@ int run_all(int dtype, const void *Q, const QueryTable &qt, int32_t d, const voi
     char *w = static_cast<char *>(ws);
     const QueryTiles tiles = single_tiles(qt.max_lq);  // (a pairs plan ignores them)
     int rc = launch_plan(offsets, lengths, B, L, qt, w, stream);
-    if (rc == MAXSIM_OK) rc = launch_score(dtype, Q, qt.max_lq, d, docs, stride, scores, L, w, tiles, stream);
-    if (rc == MAXSIM_OK) rc = launch_finish(dtype, qt.max_lq, d, scores, L, w, tiles, stream);
+    if (rc == MAXSIM_OK)
+        rc = launch_score(fmt, Q, qt.max_lq, d, docs, stride, scores, L, w, tiles, doc_scale, stream);
+    if (rc == MAXSIM_OK) rc = launch_finish(fmt, qt.max_lq, d, scores, L, w, tiles, doc_scale, stream);
     if (hipFreeAsync(ws, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
     return rc;
 }
@@ -588,7 +608,30 @@ int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, in
     if (B == 0) return MAXSIM_OK;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     if (Lq == 0) return launch_fill(scores, B, 0.0f, stream);
-    return run_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, stream);
+    return run_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, stream);
+}
+
+// Extra checks for docs stored as FP8 E4M3 bytes: whole 16-byte chunks per row and a
+// finite positive scale.
+int check_fp8(int32_t d, int64_t stride, float doc_scale)
+{
+    if (!(doc_scale > 0.0f) || doc_scale > 3.4e38f) return MAXSIM_ERR_INVALID_ARG;
+    if (d % 16 != 0 || stride % 16 != 0) return MAXSIM_ERR_UNSUPPORTED;
+    return MAXSIM_OK;
+}
+
+int rerank_fp8(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+               const int32_t *offsets, const int32_t *lengths, int32_t B, float doc_scale, float *scores,
+               void *stream_ptr)
+{
+    int st = check_common(Q, Lq, d, docs, stride, offsets, lengths, B, scores);
+    if (st != MAXSIM_OK) return st;
+    if ((st = check_fp8(d, stride, doc_scale)) != MAXSIM_OK) return st;
+    if (B == 0) return MAXSIM_OK;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    if (Lq == 0) return launch_fill(scores, B, 0.0f, stream);
+    return run_all(dtype | kFmtFp8Docs, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores,
+                   doc_scale, stream);
 }
 
 // Host checks of a query table (the per-doc checks run in the plan kernel).
@@ -620,7 +663,7 @@ int rerank_pairs(int dtype, const void *Qs, int32_t q_rows, int32_t d, const int
     st = check_common(Qs, max_lq, d, docs, stride, offsets, lengths, B, scores);
     if (st != MAXSIM_OK) return st;
     if (B == 0) return MAXSIM_OK;
-    return run_all(dtype, Qs, qt, d, docs, stride, offsets, lengths, B, scores,
+    return run_all(dtype, Qs, qt, d, docs, stride, offsets, lengths, B, scores, 1.0f,
                    static_cast<hipStream_t>(stream_ptr));
 }
 
@@ -719,11 +762,43 @@ int rerank_multi(int dtype, const void *Qs, const int32_t *q_lengths, int32_t nq
         const void *Qp = qbytes + (size_t)ps.row0 * (size_t)d * 2;
         float *sp = scores + (size_t)ps.j0 * (size_t)B;
         const int rows = ps.tiles * kTileRows;
-        rc = launch_score(dtype, Qp, rows, d, docs, stride, sp, L, w, qt, stream);
-        if (rc == MAXSIM_OK) rc = launch_finish(dtype, rows, d, sp, L, w, qt, stream);
+        rc = launch_score(dtype, Qp, rows, d, docs, stride, sp, L, w, qt, 1.0f, stream);
+        if (rc == MAXSIM_OK) rc = launch_finish(dtype, rows, d, sp, L, w, qt, 1.0f, stream);
     }
     if (hipFreeAsync(ws, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
     return rc;
+}
+
+// Bodies of the staged score and finish entries; fmt is already checked.
+int staged_score(int fmt, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                 const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, float *scores,
+                 void *workspace, size_t workspace_bytes, float doc_scale, hipStream_t s)
+{
+    const int st = check_common(Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores);
+    if (st != MAXSIM_OK) return st;
+    if (B == 0) return MAXSIM_OK;
+    if (Lq == 0) return launch_fill(scores, B, 0.0f, s);
+    if (!workspace || ((uintptr_t)workspace & 255u)) return MAXSIM_ERR_WORKSPACE;
+    Layout L;
+    if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
+    return launch_score(fmt, Q, Lq, d, docs, stride, scores, L, static_cast<char *>(workspace), single_tiles(Lq),
+                        doc_scale, s);
+}
+
+int staged_finish(int fmt, int32_t Lq, int32_t d, int32_t B, float *scores, void *workspace,
+                  size_t workspace_bytes, float doc_scale, hipStream_t s)
+{
+    if (B < 0 || Lq < 0 || d < 1) return MAXSIM_ERR_INVALID_ARG;
+    if (B > 0 && !scores) return MAXSIM_ERR_INVALID_ARG;
+    if (d > kMaxD || d % 8 != 0 || Lq > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
+    if (B > 0 && ((uintptr_t)scores & 3u)) return MAXSIM_ERR_INVALID_ARG;
+    if (B == 0 || Lq == 0) return MAXSIM_OK;
+    if (!workspace || ((uintptr_t)workspace & 255u)) return MAXSIM_ERR_WORKSPACE;
+    Layout L;
+    if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
+    return launch_finish(fmt, Lq, d, scores, L, static_cast<char *>(workspace), single_tiles(Lq), doc_scale, s);
 }
 
 }  // namespace
@@ -776,6 +851,21 @@ int maxsim_rerank_multi_bf16(const void *Qs, const int32_t *q_lengths, int32_t n
 {
     return rerank_multi(MAXSIM_BF16, Qs, q_lengths, nq, d, docs, stride, doc_offsets, doc_lengths, B, scores,
                         stream);
+}
+
+int maxsim_rerank_fp8(const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                      const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, float doc_scale,
+                      float *scores, void *stream)
+{
+    return rerank_fp8(MAXSIM_F16, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, doc_scale, scores, stream);
+}
+
+int maxsim_rerank_fp8_bf16(const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                           const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, float doc_scale,
+                           float *scores, void *stream)
+{
+    return rerank_fp8(MAXSIM_BF16, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, doc_scale, scores,
+                      stream);
 }
 
 const char *maxsim_status_string(int status)
@@ -843,33 +933,36 @@ int maxsim_score(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
                  void *workspace, size_t workspace_bytes, void *stream)
 {
     if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
-    const int st = check_common(Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores);
+    return staged_score(dtype, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores, workspace,
+                        workspace_bytes, 1.0f, static_cast<hipStream_t>(stream));
+}
+
+int maxsim_score_fp8(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                     const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, float doc_scale,
+                     float *scores, void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
+    const int st = check_fp8(d, stride, doc_scale);
     if (st != MAXSIM_OK) return st;
-    if (B == 0) return MAXSIM_OK;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (Lq == 0) return launch_fill(scores, B, 0.0f, s);
-    if (!workspace || ((uintptr_t)workspace & 255u)) return MAXSIM_ERR_WORKSPACE;
-    Layout L;
-    if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
-    if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
-    return launch_score(dtype, Q, Lq, d, docs, stride, scores, L, static_cast<char *>(workspace),
-                        single_tiles(Lq), s);
+    return staged_score(dtype | kFmtFp8Docs, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores,
+                        workspace, workspace_bytes, doc_scale, static_cast<hipStream_t>(stream));
 }
 
 int maxsim_finish(int dtype, int32_t Lq, int32_t d, int32_t B, float *scores, void *workspace,
                   size_t workspace_bytes, void *stream)
 {
     if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
-    if (B < 0 || Lq < 0 || d < 1) return MAXSIM_ERR_INVALID_ARG;
-    if (B > 0 && !scores) return MAXSIM_ERR_INVALID_ARG;
-    if (d > kMaxD || d % 8 != 0 || Lq > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
-    if (B > 0 && ((uintptr_t)scores & 3u)) return MAXSIM_ERR_INVALID_ARG;
-    if (B == 0 || Lq == 0) return MAXSIM_OK;
-    if (!workspace || ((uintptr_t)workspace & 255u)) return MAXSIM_ERR_WORKSPACE;
-    Layout L;
-    if (workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
-    if (workspace_bytes < L.total) return MAXSIM_ERR_WORKSPACE;
-    return launch_finish(dtype, Lq, d, scores, L, static_cast<char *>(workspace), single_tiles(Lq),
+    return staged_finish(dtype, Lq, d, B, scores, workspace, workspace_bytes, 1.0f,
+                         static_cast<hipStream_t>(stream));
+}
+
+int maxsim_finish_fp8(int dtype, int32_t Lq, int32_t d, int32_t B, float doc_scale, float *scores,
+                      void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
+    if (!(doc_scale > 0.0f) || doc_scale > 3.4e38f) return MAXSIM_ERR_INVALID_ARG;
+    if (d % 16 != 0) return MAXSIM_ERR_UNSUPPORTED;
+    return staged_finish(dtype | kFmtFp8Docs, Lq, d, B, scores, workspace, workspace_bytes, doc_scale,
                          static_cast<hipStream_t>(stream));
 }
 

@@ -1,5 +1,5 @@
-// MaxSim score kernel for gfx950 (CDNA4), one instance per (format, K-steps, query
-// tiles per group).
+// MaxSim score kernel for gfx950 (CDNA4), one instance per (query format, doc storage,
+// K-steps, query tiles per group).
 //
 // Operation (Flash-MaxSim rerank page, docs.vllm.ai,
 // vllm.v1.pool.flash_maxsim.flash_maxsim_rerank, module description and section
@@ -38,6 +38,10 @@
 //     valid rows, so rows past the end of the doc read as zero and are never fetched;
 //     chunks past the tile (when 16 C is not a multiple of 64) are pushed out of
 //     range the same way, and K-columns past d are zeroed in the fragment.
+//   - Docs may be stored as FP8 E4M3 (half the bytes of the bandwidth-bound stream):
+//     tiles are loaded and staged as bytes, and each lane converts its 8-byte B fragment
+//     to Q's format with the hardware converter (exact), so the MFMA and the fp32
+//     accumulation are the 16-bit path's; the doc tensor's scale multiplies the sum.
 //   - S = Qtile . Dtile^T lands with lane l holding doc row (l % 16) and query rows
 //     4 (l / 16) + j, j < 4. The accumulator of an invalid doc row (past the doc's
 //     end) starts at -inf instead of 0, which keeps it at -inf; then an element-wise
@@ -119,12 +123,36 @@ __device__ __forceinline__ uint64_t wave_uniform64(uint64_t v)
     return (uint64_t)wave_uniform((uint32_t)v) | ((uint64_t)wave_uniform((uint32_t)(v >> 32)) << 32);
 }
 
+// Eight FP8 E4M3 values (two words, lowest byte first) to the eight fp16 or bf16
+// halves of one MFMA fragment, exactly (every E4M3 value is representable in both).
+template <bool BF16>
+__device__ __forceinline__ u32x4 e4m3x8_to_16(uint32_t lo, uint32_t hi)
+{
+    u32x4 r;
+    if constexpr (BF16) {
+        r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, false));
+        r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(lo, 1.0f, true));
+        r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, false));
+        r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(hi, 1.0f, true));
+    } else {
+        r[0] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false));
+        r[1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true));
+        r[2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false));
+        r[3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true));
+    }
+    return r;
+}
+
 // MINW: waves per SIMD the register allocation must allow (512 / MINW registers).
-template <int NKS, int NQT, bool BF16, int P, int MINW>
+// BF16: element format of Q (and of the MFMA). FP8D: docs stored as FP8 E4M3 bytes
+// (converted to Q's format per fragment; the score is multiplied by a.doc_scale).
+template <int NKS, int NQT, bool BF16, bool FP8D, int P, int MINW>
 __global__ void __launch_bounds__(kScoreBlock, MINW)
 score_kernel(const ScoreArgs a)
 {
     constexpr int DPAD = NKS * kStepK;
+    // 1 KB loads per 16-row doc tile: 16 rows of d elements of 2 (or 1) bytes.
+    constexpr int NLD = FP8D ? (NKS + 1) / 2 : NKS;
     constexpr int LDQ = DPAD + 8;  // LDS row pitch (halves): 16 B skew against bank conflicts
     constexpr float NEG_INF = -__builtin_huge_valf();
 
@@ -166,14 +194,14 @@ score_kernel(const ScoreArgs a)
     const uint32_t stride_bytes = (uint32_t)a.stride_bytes;
     const int row_in_tile = lane & 15;
     const int kgroup = lane >> 4;
-    const int C = a.d / 8;           // 16-byte chunks per row
+    const int C = FP8D ? a.d / 16 : a.d / 8;  // 16-byte chunks per doc row
     const int pitch = C | 1;         // LDS row pitch in chunks
     const int dummy = kTileRows * pitch;  // LDS slot for lanes with nothing to stage
     u32x4 *tile = reinterpret_cast<u32x4 *>(qs + (a.q_in_lds ? lq_pad * LDQ : 0)) + wave * (dummy + 1);
-    uint32_t ld_off[NKS];            // byte offset in the tile of load s
-    int st_idx[NKS];                 // LDS chunk index it is staged to
+    uint32_t ld_off[NLD];            // byte offset in the tile of load s
+    int st_idx[NLD];                 // LDS chunk index it is staged to
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
+    for (int s = 0; s < NLD; ++s) {
         const int e = s * kWave + lane;
         const int row = e / C;
         const int ch = e - row * C;
@@ -182,9 +210,12 @@ score_kernel(const ScoreArgs a)
         ld_off[s] = ok ? (uint32_t)row * stride_bytes + (uint32_t)ch * 16u : (uint32_t)kTileRows * stride_bytes;
         st_idx[s] = ok ? row * pitch + ch : dummy;
     }
-    const int rd_idx = row_in_tile * pitch + kgroup;  // + 4 s for K-step s
-    // K-step NKS-1 may hold 8-column chunks past d: those fragment lanes are zero.
-    const bool last_chunk_ok = (NKS - 1) * 4 + kgroup < C;
+    // B fragment of K-step s: row row_in_tile, columns 32 s + 8 kgroup .. + 7, i.e. chunk
+    // rd_idx + 4 s (16-bit docs), or 8 bytes at rd8 + 32 s (FP8 docs).
+    const int rd_idx = row_in_tile * pitch + kgroup;
+    const int rd8 = (row_in_tile * pitch + (kgroup >> 1)) * 16 + (kgroup & 1) * 8;
+    // K-step NKS-1 may hold 8-column groups past d: those fragment lanes are zero.
+    const bool last_chunk_ok = (NKS - 1) * 4 + kgroup < a.d / 8;
 
     // Query fragments of register group grp: from LDS when the query tiles are staged
     // there, else from global memory, by the tile table or, under a pairs plan, for the
@@ -264,7 +295,7 @@ score_kernel(const ScoreArgs a)
         return sp;
     };
 
-    u32x4 buf[P][NKS];
+    u32x4 buf[P][NLD];
     // Loads of tile t of span sp into pipeline slot `slot`. The descriptor covers only
     // the tile's valid rows (none for t past the span, or for an invalid span).
     auto issue = [&](int slot, uint64_t base, int nrows, int t) {
@@ -274,7 +305,7 @@ score_kernel(const ScoreArgs a)
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             reinterpret_cast<void *>((uintptr_t)ub), (short)0, (int)wave_uniform(rows * stride_bytes), kBufferWord3);
 #pragma unroll
-        for (int s = 0; s < NKS; ++s)
+        for (int s = 0; s < NLD; ++s)
             buf[slot][s] = __builtin_bit_cast(
                 u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)ld_off[s], 0, kDocLoadPolicy));
     };
@@ -286,11 +317,17 @@ score_kernel(const ScoreArgs a)
         // Coalesced layout -> MFMA B-fragment layout through this wave's LDS buffer
         // (the LDS operations of one wave complete in order).
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) tile[st_idx[s]] = buf[slot][s];
+        for (int s = 0; s < NLD; ++s) tile[st_idx[s]] = buf[slot][s];
         u32x4 bf[NKS];
 #pragma unroll
         for (int s = 0; s < NKS; ++s) {
-            bf[s] = tile[rd_idx + 4 * s];
+            if constexpr (FP8D) {
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const char *>(tile) + rd8 + 32 * s);
+                bf[s] = e4m3x8_to_16<BF16>(v[0], v[1]);
+            } else {
+                bf[s] = tile[rd_idx + 4 * s];
+            }
             if (s == NKS - 1 && !last_chunk_ok) bf[s] = u32x4{0u, 0u, 0u, 0u};
         }
         // The accumulator starts at 0 for this lane's doc row if the row is valid and
@@ -404,9 +441,9 @@ score_kernel(const ScoreArgs a)
                     const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
                     // NaN for an invalid query, chosen and stored as bits (this code is
                     // compiled without NaN semantics for its max steps).
-                    const uint32_t v = pairs && cur.q_len < 0
-                                           ? kNaNBits
-                                           : __builtin_bit_cast(uint32_t, ((s0 + s1) + s2) + s3);
+                    float sum = ((s0 + s1) + s2) + s3;
+                    if constexpr (FP8D) sum *= a.doc_scale;
+                    const uint32_t v = pairs && cur.q_len < 0 ? kNaNBits : __builtin_bit_cast(uint32_t, sum);
                     if (lane == 0)
                         reinterpret_cast<uint32_t *>(a.scores)[(size_t)end * a.qt.score_stride + cur.doc] = v;
                     lane_sum = 0.0f;

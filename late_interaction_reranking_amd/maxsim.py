@@ -24,6 +24,10 @@ The functions carry the C ABI's names (include/maxsim.h) and take torch tensors:
     maxsim_rerank_multi_bf16(...)                               bf16
     rerank_multi(...)  picks one of the two from Qs's dtype
 
+    maxsim_rerank_fp8(Q, docs8, doc_offsets, doc_lengths, doc_scale)
+                       FP8 E4M3 docs (uint8 or float8_e4m3fn), fp16 or bf16 Q
+    maxsim_score_fp8(...), maxsim_finish_fp8(...)   staged form, after maxsim_plan
+
 Q is [Lq, d] and contiguous; docs is a 2-D view whose rows are docs.stride(0) elements
 apart with unit column stride (a column slice of a wider tensor works: its extra
 columns are never read); doc_offsets and doc_lengths are int32 [B] on the same device.
@@ -59,6 +63,9 @@ __all__ = [
     "maxsim_rerank_multi",
     "maxsim_rerank_multi_bf16",
     "rerank_multi",
+    "maxsim_rerank_fp8",
+    "maxsim_score_fp8",
+    "maxsim_finish_fp8",
     "MAXSIM_F16",
     "MAXSIM_BF16",
 ]
@@ -120,6 +127,15 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = mr
+        F32 = ctypes.c_float
+        for name in ("maxsim_rerank_fp8", "maxsim_rerank_fp8_bf16"):
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = [P, I32, I32, P, I64, P, P, I32, F32, P, P]
+        lib.maxsim_score_fp8.restype = ctypes.c_int
+        lib.maxsim_score_fp8.argtypes = [ctypes.c_int, P, I32, I32, P, I64, P, P, I32, F32, P, P, SZ, P]
+        lib.maxsim_finish_fp8.restype = ctypes.c_int
+        lib.maxsim_finish_fp8.argtypes = [ctypes.c_int, I32, I32, I32, F32, P, P, SZ, P]
         lib.maxsim_plan_pairs.restype = ctypes.c_int
         lib.maxsim_plan_pairs.argtypes = [P, P, P, I32, P, P, I32, I32, I32, I32, P, SZ, P]
         lib.maxsim_version.restype = ctypes.c_int
@@ -376,3 +392,77 @@ def rerank_multi(Qs, q_lengths, docs, doc_offsets, doc_lengths, scores=None) -> 
     """maxsim_rerank_multi or maxsim_rerank_multi_bf16, chosen by Qs's dtype."""
     fn = maxsim_rerank_multi_bf16 if Qs.dtype == torch.bfloat16 else maxsim_rerank_multi
     return fn(Qs, q_lengths, docs, doc_offsets, doc_lengths, scores)
+
+
+def _check_fp8_args(Q, docs, doc_offsets, doc_lengths):
+    if docs.dtype not in (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)):
+        raise TypeError("docs must hold FP8 E4M3 bytes (uint8 or float8_e4m3fn)")
+    if Q.dtype not in (torch.float16, torch.bfloat16):
+        raise TypeError("Q must be float16 or bfloat16")
+    if Q.dim() != 2 or docs.dim() != 2:
+        raise ValueError("Q and docs must be 2-D")
+    if doc_offsets.dtype != torch.int32 or doc_lengths.dtype != torch.int32:
+        raise TypeError("doc_offsets and doc_lengths must be int32")
+    if doc_offsets.dim() != 1 or doc_offsets.shape != doc_lengths.shape:
+        raise ValueError("doc_offsets and doc_lengths must be 1-D of equal length")
+    dev = docs.device
+    for name, t in (("Q", Q), ("docs", docs), ("doc_offsets", doc_offsets), ("doc_lengths", doc_lengths)):
+        if t.device != dev or dev.type != "cuda":
+            raise ValueError(f"{name} must live on the GPU, with docs")
+    if not Q.is_contiguous() or not doc_offsets.is_contiguous() or not doc_lengths.is_contiguous():
+        raise ValueError("Q, doc_offsets and doc_lengths must be contiguous")
+    if docs.shape[0] > 0 and docs.stride(1) != 1:
+        raise ValueError("docs must have unit column stride")
+    if Q.shape[1] != docs.shape[1]:
+        raise ValueError("Q and docs must have the same width d")
+    Lq, d = int(Q.shape[0]), int(Q.shape[1])
+    stride = int(docs.stride(0)) if docs.shape[0] > 1 else max(int(docs.stride(0)), d)
+    return Lq, d, stride, int(doc_offsets.shape[0])
+
+
+def maxsim_rerank_fp8(Q, docs, doc_offsets, doc_lengths, doc_scale: float, scores=None) -> torch.Tensor:
+    """fp32 [B] MaxSim scores with docs stored as FP8 E4M3 bytes (element = doc_scale *
+    e4m3) and an fp16 or bf16 query; d and the row stride (bytes) multiples of 16."""
+    Lq, d, stride, B = _check_fp8_args(Q, docs, doc_offsets, doc_lengths)
+    if scores is None:
+        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
+    elif scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    name = "maxsim_rerank_fp8_bf16" if Q.dtype == torch.bfloat16 else "maxsim_rerank_fp8"
+    with torch.cuda.device(docs.device):
+        st = getattr(load(), name)(Q.data_ptr(), Lq, d, docs.data_ptr(), stride, doc_offsets.data_ptr(),
+                                   doc_lengths.data_ptr(), B, float(doc_scale), scores.data_ptr(),
+                                   _stream(docs))
+    _check(st, name)
+    return scores
+
+
+def maxsim_score_fp8(Q, docs, doc_offsets, doc_lengths, doc_scale: float, workspace: torch.Tensor,
+                     scores=None) -> torch.Tensor:
+    """Staged score kernel for FP8 E4M3 docs over a schedule maxsim_plan wrote."""
+    Lq, d, stride, B = _check_fp8_args(Q, docs, doc_offsets, doc_lengths)
+    if scores is None:
+        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
+    ptr, nbytes = _ws(workspace)
+    code = MAXSIM_BF16 if Q.dtype == torch.bfloat16 else MAXSIM_F16
+    with torch.cuda.device(docs.device):
+        st = load().maxsim_score_fp8(code, Q.data_ptr(), Lq, d, docs.data_ptr(), stride, doc_offsets.data_ptr(),
+                                     doc_lengths.data_ptr(), B, float(doc_scale), scores.data_ptr(), ptr, nbytes,
+                                     _stream(docs))
+    _check(st, "maxsim_score_fp8")
+    return scores
+
+
+def maxsim_finish_fp8(Q, B: int, doc_scale: float, workspace: torch.Tensor, scores: torch.Tensor) -> torch.Tensor:
+    """Staged combine step for FP8 E4M3 docs (Q supplies Lq, d and its format)."""
+    if Q.dim() != 2:
+        raise ValueError("Q must be 2-D")
+    if scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    code = MAXSIM_BF16 if Q.dtype == torch.bfloat16 else MAXSIM_F16
+    ptr, nbytes = _ws(workspace)
+    with torch.cuda.device(workspace.device):
+        st = load().maxsim_finish_fp8(code, int(Q.shape[0]), int(Q.shape[1]), int(B), float(doc_scale),
+                                      scores.data_ptr(), ptr, nbytes, _stream(workspace))
+    _check(st, "maxsim_finish_fp8")
+    return scores

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     for n in ("maxsim_rerank", "maxsim_rerank_bf16", "maxsim_status_string",
               "maxsim_workspace_size", "maxsim_plan", "maxsim_score", "maxsim_finish",
               "maxsim_version", "maxsim_rerank_pairs", "maxsim_rerank_pairs_bf16",
-              "maxsim_plan_pairs", "maxsim_rerank_multi", "maxsim_rerank_multi_bf16"):
+              "maxsim_plan_pairs", "maxsim_rerank_multi", "maxsim_rerank_multi_bf16",
+              "maxsim_rerank_fp8", "maxsim_rerank_fp8_bf16", "maxsim_score_fp8", "maxsim_finish_fp8"):
         assert n in names
 
 
@@ -189,3 +190,39 @@ def test_multi_host_validation(lib, fn):
     assert m(nq=0, q=None) == OK
     assert m(nq=0, q=None, scores=None) == OK      # zero queries write nothing
     assert m(Qs=None, q=(ctypes.c_int32 * 3)(0, 0, 0), B=0) == OK
+
+
+@pytest.mark.parametrize("fn", ["maxsim_rerank_fp8", "maxsim_rerank_fp8_bf16"])
+@pytest.mark.parametrize("kw,code", [
+    (dict(scale=0.0), INVALID),
+    (dict(scale=-1.0), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(d=24, stride=32), UNSUPPORTED),     # d % 16
+    (dict(stride=136), UNSUPPORTED),          # stride % 16
+    (dict(d=264, stride=272), UNSUPPORTED),
+    (dict(Lq=257), UNSUPPORTED),
+    (dict(stride=64), INVALID),               # stride < d
+    (dict(docs=None), INVALID),
+    (dict(Q=FAKE + 4), UNSUPPORTED),
+    (dict(B=0, docs=None, offs=None, lens=None, scores=None), OK),
+])
+def test_fp8_host_validation(lib, fn, kw, code):
+    a = dict(Q=FAKE, Lq=32, d=128, docs=FAKE, stride=128, offs=FAKE, lens=FAKE + 1024, B=10, scale=0.01,
+             scores=FAKE + 4096)
+    a.update(kw)
+    assert getattr(lib, fn)(a["Q"], a["Lq"], a["d"], a["docs"], a["stride"], a["offs"], a["lens"], a["B"],
+                            ctypes.c_float(a["scale"]), a["scores"], None) == code
+
+
+def test_fp8_staged_validation(lib):
+    f = ctypes.c_float
+    assert lib.maxsim_score_fp8(2, FAKE, 32, 128, FAKE, 128, FAKE, FAKE, 4, f(1.0), FAKE, FAKE, 1 << 20, None) == INVALID
+    assert lib.maxsim_score_fp8(0, FAKE, 32, 128, FAKE, 128, FAKE, FAKE, 4, f(0.0), FAKE, FAKE, 1 << 20, None) == INVALID
+    assert lib.maxsim_score_fp8(0, FAKE, 32, 120, FAKE, 128, FAKE, FAKE, 4, f(1.0), FAKE, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert lib.maxsim_score_fp8(0, FAKE, 32, 128, FAKE, 128, FAKE, FAKE, 4, f(1.0), FAKE, None, 1 << 20, None) == WORKSPACE
+    assert lib.maxsim_score_fp8(1, FAKE, 32, 128, FAKE, 128, FAKE, FAKE, 0, f(1.0), None, None, 0, None) == OK
+    assert lib.maxsim_finish_fp8(0, 32, 128, 4, f(-2.0), FAKE, FAKE, 1 << 20, None) == INVALID
+    assert lib.maxsim_finish_fp8(0, 32, 120, 4, f(1.0), FAKE, FAKE, 1 << 20, None) == UNSUPPORTED
+    assert lib.maxsim_finish_fp8(0, 32, 128, 4, f(1.0), FAKE, None, 1 << 20, None) == WORKSPACE
+    assert lib.maxsim_finish_fp8(0, 32, 128, 0, f(1.0), None, None, 0, None) == OK
