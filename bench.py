@@ -96,6 +96,26 @@ def algorithmic_flops(w) -> float:
     return 2.0 * w.Lq * w.d * w.doc_tokens
 
 
+def score_launches(w) -> int:
+    """Score launches of one maxsim_rerank_multi call: queries are packed in order into
+    passes of at most one register group of 16-row query tiles (min(32 // ceil(d / 32), 8)
+    tiles), a longer query alone; 1 for the other workload forms."""
+    if not w.shared_docs:
+        return 1
+    group = min(32 // -(-w.d // 32), 8)
+    passes, cur = 0, 0
+    for L in (int(x) for x in w.q_lengths):
+        t = -(-L // 16)
+        if t == 0:
+            continue
+        if cur and cur + t > group:
+            passes, cur = passes + 1, 0
+        cur += t
+        if cur >= group:
+            passes, cur = passes + 1, 0
+    return passes + (1 if cur else 0)
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as fh:
@@ -158,22 +178,15 @@ def _top10_ok(g, ref) -> bool:
 
 
 def parity_summary(gpu, ref, w):
-    """Scores of the timed run against the oracle (docs 0 .. len(ref) - 1), under the
-    acceptance rule |gpu - oracle| <= 1e-3 (1 + |oracle|). The top-10 check needs every
-    doc of a ranking scored: the whole batch for one query, else each query whose docs
-    were all checked."""
+    """Scores of the timed run against the oracle (docs 0 .. n-1 that the CPU baseline
+    scored), under the acceptance rule |gpu - oracle| <= 1e-3 (1 + |oracle|). The top-10
+    check needs every doc of a ranking scored: the whole batch for one query (or for
+    each query sharing the docs), else each query of a pairs batch whose docs were all
+    checked."""
     import numpy as np
 
-    n = len(ref)
-    g = np.asarray(gpu[:n], np.float64)
-    inf = np.isinf(ref)
-    fin = ~inf
-    err = np.abs(g[fin] - ref[fin]) / (1.0 + np.abs(ref[fin]))
-    bad = int(np.sum(~(err <= 1e-3))) + int(np.sum(g[inf] != ref[inf]))
-    out = {"docs_checked": int(n), "max_scaled_err": float(err.max()) if err.size else 0.0,
-           "violations": bad, "top10_ok": None}
     if w.shared_docs:
-        # ref: [nq, n] for docs 0 .. n-1
+        # ref: [nq, n]
         n = ref.shape[1]
         g = np.asarray(gpu, np.float64)[:, :n]
         inf = np.isinf(ref)
@@ -185,6 +198,14 @@ def parity_summary(gpu, ref, w):
         if n == w.B:
             out["top10_ok"] = bool(all(_top10_ok(g[j], ref[j]) for j in range(ref.shape[0])))
         return out
+    n = len(ref)
+    g = np.asarray(gpu[:n], np.float64)
+    inf = np.isinf(ref)
+    fin = ~inf
+    err = np.abs(g[fin] - ref[fin]) / (1.0 + np.abs(ref[fin]))
+    bad = int(np.sum(~(err <= 1e-3))) + int(np.sum(g[inf] != ref[inf]))
+    out = {"docs_checked": int(n), "max_scaled_err": float(err.max()) if err.size else 0.0,
+           "violations": bad, "top10_ok": None}
     if not w.multi_query:
         if n == w.B:
             out["top10_ok"] = _top10_ok(g, ref)
@@ -207,6 +228,8 @@ def main() -> int:
                     choices=["tiny", "colbert", "long_doc", "scattered", "large", "pairs", "shared",
                              "large_fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--topk", type=int, default=0,
+                    help="also select the k best docs on the GPU in every step (maxsim_topk)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one plain 2 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -257,8 +280,18 @@ def main() -> int:
     else:
         def plan():
             lir.maxsim_plan(offs, lens, w.Lq, w.d, ws)
+    if args.topk:
+        if w.shared_docs or w.multi_query:
+            print("--topk applies to single-query workloads", file=sys.stderr)
+            return 2
+        import ctypes
+
+        nb = ctypes.c_size_t(0)
+        lir.load().maxsim_topk_workspace_size(w.B, args.topk, ctypes.byref(nb))
+        tk_ws = torch.empty(int(nb.value), dtype=torch.uint8, device=dev)
     torch.cuda.synchronize()
     log("uploaded")
+    tk_events = []
 
     def step(ev_a=None, ev_b=None):
         if w.shared_docs:
@@ -281,6 +314,14 @@ def main() -> int:
             lir.maxsim_finish_fp8(Q, w.B, w.doc_scale, ws, scores)
         else:
             lir.maxsim_finish(Q, w.B, ws, scores, Lq=w.Lq)
+        if args.topk:
+            if ev_a is not None:
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+            lir.maxsim_topk(scores, args.topk, tk_ws)
+            if ev_a is not None:
+                e1.record()
+                tk_events.append((e0, e1))
 
     for _ in range(args.warmup):
         step()
@@ -314,7 +355,13 @@ def main() -> int:
         del src, dst
 
     alg_bytes = algorithmic_bytes(w)
-    achieved = alg_bytes / (score_avg_ms * 1e-3) / 1e9
+    launches = score_launches(w)
+    # Per score launch: one maxsim_rerank_multi call holds `launches` score launches, each
+    # reading the docs once (its events bracket the whole call, plan and combines too).
+    launch_bytes = alg_bytes if launches == 1 else w.doc_bytes + w.B * (8 + 4 * w.nq // launches) + (
+        w.Q.shape[0] * w.d * 2 // launches)
+    launch_ms = score_avg_ms / launches
+    achieved = launch_bytes / (launch_ms * 1e-3) / 1e9
     flops = algorithmic_flops(w)
     scored_tokens = w.doc_tokens * (w.nq if w.shared_docs else 1)
     tokens_per_s = scored_tokens / (ms_per_step * 1e-3)
@@ -347,19 +394,23 @@ def main() -> int:
         "mfma_util_algorithmic": flops / (score_avg_ms * 1e-3) / (MFMA_F16_PEAK_TFLOPS * 1e12),
         "roofline": {
             "bound": "hbm",
-            "kernel": ("maxsim_rerank_multi call (plan + per pass score + combine)" if w.shared_docs
-                       else "score_kernel"),
+            "kernel": ("score_kernel (per pass: the maxsim_rerank_multi call's time, plan and combines "
+                       "included, over its score launches)" if w.shared_docs else "score_kernel"),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
             "traffic": measured_traffic(w.name),
-            "algorithmic_bytes_per_launch": alg_bytes,
-            "avg_launch_ms": score_avg_ms,
+            "algorithmic_bytes_per_launch": launch_bytes,
+            "avg_launch_ms": launch_ms,
+            "launches_per_step": launches,
         },
         "cpu_baseline": None,
         "parity": None,
     }
+    if args.topk:
+        tk_ms = [a.elapsed_time(b) for a, b in tk_events]
+        rec["topk"] = {"k": args.topk, "avg_ms": sum(tk_ms) / len(tk_ms), "included_in_step": True}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         rec["cpu_baseline"], ref = cpu_baseline(w)

@@ -180,6 +180,40 @@ MAXSIM_API int maxsim_rerank_fp8_bf16(const void *Q, int32_t Lq, int32_t d,
                            const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
                            float doc_scale, float *scores, void *stream);
 
+/*
+ * Top-k of a score array on the GPU (the rerank's consumer: the Flash-MaxSim rerank page
+ * returns raw per-doc scores, `flash_maxsim_rerank_direct` return value, and the caller
+ * keeps the best docs). Order: score descending; equal scores (-0 equal to +0) by
+ * lower doc index; NaN after every number; so the k results are unique.
+ *
+ * scores:     fp32 [B] (device).
+ * k:          0 <= k <= 1024 (MAXSIM_ERR_UNSUPPORTED above).
+ * top_scores: fp32 [k] (device): the selected scores, bit for bit as in `scores`.
+ * top_ids:    int32 [k] (device): their indices; slots past B hold (-inf, -1).
+ * workspace:  device, 256-byte aligned, maxsim_topk_workspace_size(B, k) bytes.
+ * Enqueued on `stream` without host synchronisation.
+ */
+MAXSIM_API int maxsim_topk_workspace_size(int32_t B, int32_t k, size_t *bytes);
+
+MAXSIM_API int maxsim_topk(const float *scores, int32_t B, int32_t k, float *top_scores,
+                int32_t *top_ids, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * maxsim_rerank followed by maxsim_topk in one call: the scores stay in a stream-ordered
+ * temporary buffer and only the k best (score, doc index) pairs are written. Arguments
+ * as for maxsim_rerank and maxsim_topk.
+ */
+MAXSIM_API int maxsim_rerank_topk(const void *Q, int32_t Lq, int32_t d,
+                       const void *docs, int64_t stride,
+                       const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                       int32_t k, float *top_scores, int32_t *top_ids, void *stream);
+
+/* Same as maxsim_rerank_topk, bf16 Q and docs. */
+MAXSIM_API int maxsim_rerank_topk_bf16(const void *Q, int32_t Lq, int32_t d,
+                            const void *docs, int64_t stride,
+                            const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                            int32_t k, float *top_scores, int32_t *top_ids, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 MAXSIM_API const char *maxsim_status_string(int status);
 

@@ -28,6 +28,8 @@ from .maxsim import (  # noqa: F401
     maxsim_rerank_multi_bf16,
     maxsim_rerank_pairs,
     maxsim_rerank_pairs_bf16,
+    maxsim_rerank_topk,
+    maxsim_topk,
     maxsim_finish,
     maxsim_finish_fp8,
     maxsim_rerank_fp8,

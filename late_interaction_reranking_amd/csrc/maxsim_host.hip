@@ -7,6 +7,7 @@
 
 #include "maxsim_common.h"
 #include "maxsim_sched.h"
+#include "maxsim_topk.h"
 
 using namespace maxsim;
 
@@ -611,6 +612,37 @@ int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, in
     return run_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, stream);
 }
 
+// Scores into a stream-ordered temporary buffer, then the device top-k of them.
+int rerank_topk(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                const int32_t *offsets, const int32_t *lengths, int32_t B, int32_t k, float *top_scores,
+                int32_t *top_ids, void *stream_ptr)
+{
+    if (k < 0) return MAXSIM_ERR_INVALID_ARG;
+    if (k > kTopkMaxK) return MAXSIM_ERR_UNSUPPORTED;
+    if (k > 0 && (!top_scores || !top_ids)) return MAXSIM_ERR_INVALID_ARG;
+    if (((uintptr_t)top_scores | (uintptr_t)top_ids) & 3u) return MAXSIM_ERR_INVALID_ARG;
+    // The score arguments are checked as maxsim_rerank checks them (scores is internal).
+    int st = check_common(Q, Lq, d, docs, stride, offsets, lengths, B, nullptr, false);
+    if (st != MAXSIM_OK) return st;
+    if (k == 0) return MAXSIM_OK;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    const size_t score_bytes = ((size_t)(B > 0 ? B : 1) * 4 + 255) & ~size_t(255);
+    void *buf = nullptr;
+    if (hipMallocAsync(&buf, score_bytes + topk_workspace_bytes(B, k), stream) != hipSuccess) return MAXSIM_ERR_HIP;
+    float *scores = static_cast<float *>(buf);
+    int rc = MAXSIM_OK;
+    if (B > 0) {
+        if (Lq == 0)
+            rc = launch_fill(scores, B, 0.0f, stream);
+        else
+            rc = run_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, stream);
+    }
+    if (rc == MAXSIM_OK)
+        rc = launch_topk(scores, B, k, top_scores, top_ids, static_cast<char *>(buf) + score_bytes, stream);
+    if (hipFreeAsync(buf, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
+    return rc;
+}
+
 // Extra checks for docs stored as FP8 E4M3 bytes: whole 16-byte chunks per row and a
 // finite positive scale.
 int check_fp8(int32_t d, int64_t stride, float doc_scale)
@@ -866,6 +898,22 @@ int maxsim_rerank_fp8_bf16(const void *Q, int32_t Lq, int32_t d, const void *doc
 {
     return rerank_fp8(MAXSIM_BF16, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, doc_scale, scores,
                       stream);
+}
+
+int maxsim_rerank_topk(const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                       const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, int32_t k,
+                       float *top_scores, int32_t *top_ids, void *stream)
+{
+    return rerank_topk(MAXSIM_F16, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, k, top_scores, top_ids,
+                       stream);
+}
+
+int maxsim_rerank_topk_bf16(const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                            const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, int32_t k,
+                            float *top_scores, int32_t *top_ids, void *stream)
+{
+    return rerank_topk(MAXSIM_BF16, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, k, top_scores, top_ids,
+                       stream);
 }
 
 const char *maxsim_status_string(int status)

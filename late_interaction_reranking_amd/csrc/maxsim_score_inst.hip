@@ -20,26 +20,45 @@ constexpr int NKS = MAXSIM_NKS;
 constexpr bool BF = MAXSIM_BF16 != 0;
 constexpr bool FP8 = MAXSIM_FP8 != 0;
 constexpr int NLD = FP8 ? (NKS + 1) / 2 : NKS;  // 1 KB loads per doc tile
-// Pipeline depth in doc tiles: 4-8 KB of coalesced loads outstanding per wave (FP8
-// tiles are half the bytes, so twice as many).
-#ifdef MAXSIM_FORCE_P
-constexpr int P = MAXSIM_FORCE_P;
-#else
-constexpr int P16 = NKS >= 3 ? 2 : (NKS == 2 ? 3 : 4);
-constexpr int P = FP8 ? (2 * P16 < 8 ? 2 * P16 : 8) : P16;
-#endif
+// Register estimate of one wave: query fragments, P tiles of loads in flight, one
+// staged fragment set, running maxima and accumulators, plus addressing and loop state.
+template <int NQT>
+constexpr int reg_estimate(int p)
+{
+    return 4 * NQT * NKS + 4 * p * NLD + 4 * NKS + 4 * NQT + 48;
+}
 
-// Occupancy target (waves per SIMD) from an estimate of the registers one wave needs:
-// query fragments, P tiles of loads in flight, one staged fragment set, running
-// maxima and accumulators, plus addressing and loop state.
+// Waves per SIMD that a register need allows (512 / waves registers each).
+constexpr int waves_for(int regs) { return regs <= 128 ? 4 : (regs <= 168 ? 3 : (regs <= 256 ? 2 : 1)); }
+
+// Pipeline depth in doc tiles: at least 4-8 KB of coalesced loads in flight per wave
+// (FP8 tiles are half the bytes, so twice as many), then deeper while the instance
+// keeps the occupancy it has at that depth (up to 4 tiles of 16-bit docs).
+template <int NQT>
+constexpr int pipe_depth()
+{
+#ifdef MAXSIM_FORCE_P
+    return MAXSIM_FORCE_P;
+#else
+    constexpr int base16 = NKS >= 3 ? 2 : (NKS == 2 ? 3 : 4);
+    if constexpr (FP8) {
+        return 2 * base16 < 8 ? 2 * base16 : 8;
+    } else {
+        int p = base16;
+        while (p < 4 && waves_for(reg_estimate<NQT>(p + 1)) == waves_for(reg_estimate<NQT>(base16))) ++p;
+        return p;
+    }
+#endif
+}
+
+// Occupancy target (waves per SIMD) for the register allocation.
 template <int NQT>
 constexpr int min_waves()
 {
 #ifdef MAXSIM_FORCE_MINW
     return MAXSIM_FORCE_MINW;
 #else
-    constexpr int est = 4 * NQT * NKS + 4 * P * NLD + 4 * NKS + 4 * NQT + 48;
-    return est <= 128 ? 4 : (est <= 168 ? 3 : (est <= 256 ? 2 : 1));
+    return waves_for(reg_estimate<NQT>(pipe_depth<NQT>()));
 #endif
 }
 
@@ -47,7 +66,8 @@ template <int NQT>
 const void *entry()
 {
     if constexpr (NQT * NKS <= maxsim::kMaxFragsPerGroup)
-        return reinterpret_cast<const void *>(&maxsim::score_kernel<NKS, NQT, BF, FP8, P, min_waves<NQT>()>);
+        return reinterpret_cast<const void *>(
+            &maxsim::score_kernel<NKS, NQT, BF, FP8, pipe_depth<NQT>(), min_waves<NQT>()>);
     else
         return nullptr;
 }

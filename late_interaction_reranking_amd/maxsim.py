@@ -28,6 +28,9 @@ The functions carry the C ABI's names (include/maxsim.h) and take torch tensors:
                        FP8 E4M3 docs (uint8 or float8_e4m3fn), fp16 or bf16 Q
     maxsim_score_fp8(...), maxsim_finish_fp8(...)   staged form, after maxsim_plan
 
+    maxsim_topk(scores, k) -> (top_scores [k], top_ids [k])   device top-k
+    maxsim_rerank_topk(Q, docs, doc_offsets, doc_lengths, k)  scores + top-k, one call
+
 Q is [Lq, d] and contiguous; docs is a 2-D view whose rows are docs.stride(0) elements
 apart with unit column stride (a column slice of a wider tensor works: its extra
 columns are never read); doc_offsets and doc_lengths are int32 [B] on the same device.
@@ -66,6 +69,8 @@ __all__ = [
     "maxsim_rerank_fp8",
     "maxsim_score_fp8",
     "maxsim_finish_fp8",
+    "maxsim_topk",
+    "maxsim_rerank_topk",
     "MAXSIM_F16",
     "MAXSIM_BF16",
 ]
@@ -136,6 +141,14 @@ def load() -> ctypes.CDLL:
         lib.maxsim_score_fp8.argtypes = [ctypes.c_int, P, I32, I32, P, I64, P, P, I32, F32, P, P, SZ, P]
         lib.maxsim_finish_fp8.restype = ctypes.c_int
         lib.maxsim_finish_fp8.argtypes = [ctypes.c_int, I32, I32, I32, F32, P, P, SZ, P]
+        lib.maxsim_topk_workspace_size.restype = ctypes.c_int
+        lib.maxsim_topk_workspace_size.argtypes = [I32, I32, ctypes.POINTER(SZ)]
+        lib.maxsim_topk.restype = ctypes.c_int
+        lib.maxsim_topk.argtypes = [P, I32, I32, P, P, P, SZ, P]
+        for name in ("maxsim_rerank_topk", "maxsim_rerank_topk_bf16"):
+            fn = getattr(lib, name)
+            fn.restype = ctypes.c_int
+            fn.argtypes = [P, I32, I32, P, I64, P, P, I32, I32, P, P, P]
         lib.maxsim_plan_pairs.restype = ctypes.c_int
         lib.maxsim_plan_pairs.argtypes = [P, P, P, I32, P, P, I32, I32, I32, I32, P, SZ, P]
         lib.maxsim_version.restype = ctypes.c_int
@@ -466,3 +479,47 @@ def maxsim_finish_fp8(Q, B: int, doc_scale: float, workspace: torch.Tensor, scor
                                       scores.data_ptr(), ptr, nbytes, _stream(workspace))
     _check(st, "maxsim_finish_fp8")
     return scores
+
+
+def maxsim_topk(scores: torch.Tensor, k: int, workspace: torch.Tensor | None = None):
+    """(top_scores fp32 [k], top_ids int32 [k]) of a contiguous fp32 score vector on the
+    GPU: score descending, ties by lower index, NaN last; (-inf, -1) past the end."""
+    if scores.dtype != torch.float32 or scores.dim() != 1 or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous 1-D float32 tensor")
+    if scores.device.type != "cuda":
+        raise ValueError("scores must live on the GPU")
+    B, k = int(scores.shape[0]), int(k)
+    if k < 0:
+        raise ValueError("k must be >= 0")
+    dev = scores.device
+    n = ctypes.c_size_t(0)
+    _check(load().maxsim_topk_workspace_size(B, k, ctypes.byref(n)), "maxsim_topk_workspace_size")
+    if workspace is None:
+        workspace = torch.empty(int(n.value), dtype=torch.uint8, device=dev)
+    ptr, nbytes = _ws(workspace)
+    top_scores = torch.empty(k, dtype=torch.float32, device=dev)
+    top_ids = torch.empty(k, dtype=torch.int32, device=dev)
+    with torch.cuda.device(dev):
+        st = load().maxsim_topk(scores.data_ptr(), B, k, top_scores.data_ptr(), top_ids.data_ptr(), ptr, nbytes,
+                                _stream(scores))
+    _check(st, "maxsim_topk")
+    return top_scores, top_ids
+
+
+def maxsim_rerank_topk(Q, docs, doc_offsets, doc_lengths, k: int):
+    """The k best docs of a single-query rerank, (top_scores [k], top_ids [k]), without
+    materialising the scores outside the library (fp16 or bf16 from Q's dtype)."""
+    dtype = torch.bfloat16 if Q.dtype == torch.bfloat16 else torch.float16
+    Lq, d, stride, B = _marshal(Q, docs, doc_offsets, doc_lengths, dtype)
+    k = int(k)
+    if k < 0:
+        raise ValueError("k must be >= 0")
+    top_scores = torch.empty(k, dtype=torch.float32, device=docs.device)
+    top_ids = torch.empty(k, dtype=torch.int32, device=docs.device)
+    name = "maxsim_rerank_topk_bf16" if dtype == torch.bfloat16 else "maxsim_rerank_topk"
+    with torch.cuda.device(docs.device):
+        st = getattr(load(), name)(Q.data_ptr(), Lq, d, docs.data_ptr(), stride, doc_offsets.data_ptr(),
+                                   doc_lengths.data_ptr(), B, k, top_scores.data_ptr(), top_ids.data_ptr(),
+                                   _stream(docs))
+    _check(st, name)
+    return top_scores, top_ids

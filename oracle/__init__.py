@@ -34,6 +34,11 @@ tests/test_oracle_golden.py and tests/test_oracle_mutants.py):
   (`stage_prefill_pages`). The decoder is pinned on all 256 patterns against torch's
   float8_e4m3fn; the score by exact brute force, one-hot closed forms and the
   equality with ``maxsim`` on the decoded values (tests/test_oracle_fp8.py).
+- ``topk(scores, k)``: the k best docs of a score array under the ranking rule (score
+  descending, ties by lower doc index; -0 ties with +0, NaN ranks below everything,
+  -inf below every finite score); past B the slots hold (-inf, -1). A plain sort,
+  pinned by pairwise brute force on small arrays with ties, zeros of both signs,
+  infinities and NaN (tests/test_oracle_topk.py).
 """
 
 from __future__ import annotations
@@ -46,7 +51,7 @@ import threading
 import numpy as np
 
 __all__ = ["FMT", "build", "Oracle", "decode", "decode_e4m3", "maxsim", "maxsim_fp8",
-           "maxsim_pairs", "maxsim_multi", "maxsim_workload", "max_threads"]
+           "maxsim_pairs", "maxsim_multi", "maxsim_workload", "max_threads", "topk"]
 
 FMT = {"f16": 0, "bf16": 1}
 
@@ -263,3 +268,21 @@ def maxsim_workload(w, docs=None, threads: int = 0) -> np.ndarray:
 
 def max_threads() -> int:
     return int(_get().lib.oracle_max_threads())
+
+
+def topk(scores, k: int):
+    """(top_scores, top_ids) of the k best entries of a float32 score array: higher score
+    first, equal scores (-0 equal to +0) by lower index, NaN after everything. Slots
+    past the array's end hold (-inf, -1)."""
+    vals = np.asarray(scores, dtype=np.float32)
+
+    def rank_key(i):
+        v = float(vals[i])
+        return (1, 0.0, i) if v != v else (0, -v, i)  # NaN last; 0.0 == -0.0 compare equal
+
+    order = sorted(range(vals.shape[0]), key=rank_key)[:k]
+    top_ids = np.full(k, -1, np.int32)
+    top_scores = np.full(k, -np.inf, np.float32)
+    top_ids[: len(order)] = order
+    top_scores[: len(order)] = vals[order]
+    return top_scores, top_ids

@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
               "maxsim_workspace_size", "maxsim_plan", "maxsim_score", "maxsim_finish",
               "maxsim_version", "maxsim_rerank_pairs", "maxsim_rerank_pairs_bf16",
               "maxsim_plan_pairs", "maxsim_rerank_multi", "maxsim_rerank_multi_bf16",
-              "maxsim_rerank_fp8", "maxsim_rerank_fp8_bf16", "maxsim_score_fp8", "maxsim_finish_fp8"):
+              "maxsim_rerank_fp8", "maxsim_rerank_fp8_bf16", "maxsim_score_fp8", "maxsim_finish_fp8",
+              "maxsim_topk_workspace_size", "maxsim_topk", "maxsim_rerank_topk", "maxsim_rerank_topk_bf16"):
         assert n in names
 
 
@@ -226,3 +227,43 @@ def test_fp8_staged_validation(lib):
     assert lib.maxsim_finish_fp8(0, 32, 120, 4, f(1.0), FAKE, FAKE, 1 << 20, None) == UNSUPPORTED
     assert lib.maxsim_finish_fp8(0, 32, 128, 4, f(1.0), FAKE, None, 1 << 20, None) == WORKSPACE
     assert lib.maxsim_finish_fp8(0, 32, 128, 0, f(1.0), None, None, 0, None) == OK
+
+
+def test_topk_validation(lib):
+    n = ctypes.c_size_t(0)
+    assert lib.maxsim_topk_workspace_size(100, 10, ctypes.byref(n)) == OK and n.value >= 256
+    assert lib.maxsim_topk_workspace_size(80000, 100, ctypes.byref(n)) == OK
+    assert n.value >= 2 * 20 * 100 * 8
+    assert lib.maxsim_topk_workspace_size(-1, 10, ctypes.byref(n)) == INVALID
+    assert lib.maxsim_topk_workspace_size(10, 1025, ctypes.byref(n)) == UNSUPPORTED
+    assert lib.maxsim_topk_workspace_size(10, 10, None) == INVALID
+
+    def tk(scores=FAKE, B=100, k=10, ts=FAKE + 4096, ti=FAKE + 8192, ws=FAKE + 65536, nb=1 << 20):
+        return lib.maxsim_topk(scores, B, k, ts, ti, ws, nb, None)
+
+    assert tk(k=-1) == INVALID
+    assert tk(B=-1) == INVALID
+    assert tk(k=1025) == UNSUPPORTED
+    assert tk(k=0, scores=None, ts=None, ti=None, ws=None) == OK
+    assert tk(scores=None) == INVALID
+    assert tk(ts=None) == INVALID
+    assert tk(ti=FAKE + 2) == INVALID
+    assert tk(ws=None) == WORKSPACE
+    assert tk(ws=FAKE + 128) == WORKSPACE
+    assert tk(B=80000, k=100, nb=256) == WORKSPACE
+
+
+@pytest.mark.parametrize("fn", ["maxsim_rerank_topk", "maxsim_rerank_topk_bf16"])
+def test_rerank_topk_validation(lib, fn):
+    def rt(Q=FAKE, Lq=32, d=128, docs=FAKE, stride=128, offs=FAKE, lens=FAKE + 1024, B=10, k=5,
+           ts=FAKE + 4096, ti=FAKE + 8192):
+        return getattr(lib, fn)(Q, Lq, d, docs, stride, offs, lens, B, k, ts, ti, None)
+
+    assert rt(k=-1) == INVALID
+    assert rt(k=1025) == UNSUPPORTED
+    assert rt(ts=None) == INVALID
+    assert rt(ti=FAKE + 1) == INVALID
+    assert rt(d=12, stride=16) == UNSUPPORTED
+    assert rt(docs=None) == INVALID
+    assert rt(B=-1) == INVALID
+    assert rt(k=0, ts=None, ti=None) == OK
