@@ -49,7 +49,7 @@ topk_level_kernel(const float *__restrict__ scores, const uint64_t *__restrict__
     __shared__ uint32_t hist[256];
     __shared__ uint64_t sel[kTopkMaxK];  // the final level's survivors
     __shared__ uint64_t sh_prefix, sh_and, sh_or;
-    __shared__ uint32_t sh_need, sh_cnt;
+    __shared__ uint32_t sh_need, sh_cnt, sh_done;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
 
@@ -80,6 +80,7 @@ topk_level_kernel(const float *__restrict__ scores, const uint64_t *__restrict__
         sh_or = 0;
         sh_need = (uint32_t)k;
         sh_cnt = 0u;
+        sh_done = 0u;
     }
     __syncthreads();
     if (lane == 0) {
@@ -94,7 +95,9 @@ topk_level_kernel(const float *__restrict__ scores, const uint64_t *__restrict__
     __syncthreads();
 
     // Radix selection of the k-th largest key, 8 bits per pass below the common bits:
-    // `prefix` holds its bits above the current digit.
+    // `prefix` holds its bits above the current digit. It stops early when the chosen
+    // bin holds exactly the keys still needed: then every key whose bits under `mask`
+    // reach `prefix` is selected, without resolving the rest of the threshold.
     for (int hi = top; hi > 0; hi -= 8) {
         const int shift = hi >= 8 ? hi - 8 : 0;
         const uint32_t dmask = (1u << (hi - shift)) - 1u;
@@ -128,6 +131,7 @@ topk_level_kernel(const float *__restrict__ scores, const uint64_t *__restrict__
                     if (acc + c[i] >= need) {
                         sh_prefix = prefix | ((uint64_t)(255 - 4 * lane - i) << shift);
                         sh_need = need - acc;
+                        if (acc + c[i] == need) sh_done = 1u;
                         break;
                     }
                     acc += c[i];
@@ -136,19 +140,21 @@ topk_level_kernel(const float *__restrict__ scores, const uint64_t *__restrict__
         }
         mask |= (uint64_t)dmask << shift;
         __syncthreads();
+        if (sh_done) break;
     }
 
-    // Keep the keys above T, then fill the remaining places with keys equal to T (only
-    // the zero padding can repeat).
+    // Keep the keys above the threshold prefix, then fill the remaining places with keys
+    // on it (after an early stop they fill them exactly; after a full selection only the
+    // zero padding can repeat the threshold key).
     const uint64_t T = sh_prefix;
     uint64_t *dst = out_keys ? out_keys + (int64_t)blockIdx.x * k : sel;
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-        if (key[j] > T) dst[atomicAdd(&sh_cnt, 1u)] = key[j];
+        if ((key[j] & mask) > T) dst[atomicAdd(&sh_cnt, 1u)] = key[j];
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < PER; ++j)
-        if (key[j] == T) {
+        if ((key[j] & mask) == T) {
             const uint32_t pos = atomicAdd(&sh_cnt, 1u);
             if (pos < (uint32_t)k) dst[pos] = key[j];
         }
