@@ -16,7 +16,8 @@ holding a planted near-duplicate of a query row.
 (maxsim_rerank_multi, one call: plan, then per pass of 128 query rows a score and a
 combine launch); its events bracket the whole call, and a doc token counts once per
 query that scores it. --workload large_fp8 times the large workload with docs stored as
-FP8 E4M3 bytes (scale 2^-8; maxsim_plan, maxsim_score_fp8, maxsim_finish_fp8).
+FP8 E4M3 bytes (scale 2^-8; maxsim_plan, maxsim_score_fp8, maxsim_finish_fp8), and
+--workload shared_fp8 the shared workload with FP8 docs (maxsim_rerank_multi_fp8).
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload large]
                     [--no-cpu-baseline] [--copy-probe]
@@ -226,7 +227,7 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="large",
                     choices=["tiny", "colbert", "long_doc", "scattered", "large", "pairs", "shared",
-                             "large_fp8"])
+                             "large_fp8", "shared_fp8"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--topk", type=int, default=0,
                     help="also select the k best docs on the GPU in every step (maxsim_topk)")
@@ -297,7 +298,10 @@ def main() -> int:
         if w.shared_docs:
             if ev_a is not None:
                 ev_a.record()
-            lir.rerank_multi(Q, q_lengths, X, offs, lens, scores=scores)
+            if w.X8 is not None:
+                lir.maxsim_rerank_multi_fp8(Q, q_lengths, X, offs, lens, w.doc_scale, scores=scores)
+            else:
+                lir.rerank_multi(Q, q_lengths, X, offs, lens, scores=scores)
             if ev_b is not None:
                 ev_b.record()
             return

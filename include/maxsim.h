@@ -214,6 +214,24 @@ MAXSIM_API int maxsim_rerank_topk_bf16(const void *Q, int32_t Lq, int32_t d,
                             const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
                             int32_t k, float *top_scores, int32_t *top_ids, void *stream);
 
+/*
+ * The pairs batch and the shared-doc multi-query form over FP8 E4M3 docs with one scale
+ * (the operations of maxsim_rerank_pairs and maxsim_rerank_multi, doc elements as in
+ * maxsim_rerank_fp8). dtype is the query format, MAXSIM_F16 or MAXSIM_BF16
+ * (MAXSIM_ERR_INVALID_ARG otherwise); the FP8 envelope and scale checks apply.
+ */
+MAXSIM_API int maxsim_rerank_pairs_fp8(int dtype, const void *Qs, int32_t q_rows, int32_t d,
+                            const int32_t *q_offsets, const int32_t *q_lengths, int32_t nq,
+                            int32_t max_lq, const void *docs, int64_t stride,
+                            const int32_t *doc_offsets, const int32_t *doc_lengths,
+                            const int32_t *doc_query, int32_t B, float doc_scale, float *scores,
+                            void *stream);
+
+MAXSIM_API int maxsim_rerank_multi_fp8(int dtype, const void *Qs, const int32_t *q_lengths,
+                            int32_t nq, int32_t d, const void *docs, int64_t stride,
+                            const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                            float doc_scale, float *scores, void *stream);
+
 /* Static, NUL-terminated description of a status code (never NULL). */
 MAXSIM_API const char *maxsim_status_string(int status);
 

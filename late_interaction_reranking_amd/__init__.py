@@ -26,8 +26,10 @@ from .maxsim import (  # noqa: F401
     maxsim_rerank_bf16,
     maxsim_rerank_multi,
     maxsim_rerank_multi_bf16,
+    maxsim_rerank_multi_fp8,
     maxsim_rerank_pairs,
     maxsim_rerank_pairs_bf16,
+    maxsim_rerank_pairs_fp8,
     maxsim_rerank_topk,
     maxsim_topk,
     maxsim_finish,

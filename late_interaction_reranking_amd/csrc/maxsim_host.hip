@@ -1,5 +1,8 @@
 // C ABI of the MaxSim rerank library (declared in include/maxsim.h): argument checks,
-// the plan (length-binned doc schedule) kernels, and the launch of the score kernel.
+// the plan (length-binned doc schedule) kernels, the combine kernel (split docs), and
+// the launches of the score kernel for every entry point: one query, a pairs batch
+// (each doc with its own query), several queries over the same docs (passes of query
+// tiles), and FP8 E4M3 docs. The top-k selection lives in maxsim_topk.hip.
 #include "maxsim.h"
 
 #include <mutex>
@@ -684,18 +687,20 @@ int check_queries(const int32_t *q_offsets, const int32_t *q_lengths, int32_t nq
     return MAXSIM_OK;
 }
 
-int rerank_pairs(int dtype, const void *Qs, int32_t q_rows, int32_t d, const int32_t *q_offsets,
+// fmt: kernel format (query format, | kFmtFp8Docs for FP8 E4M3 docs with doc_scale).
+int rerank_pairs(int fmt, const void *Qs, int32_t q_rows, int32_t d, const int32_t *q_offsets,
                  const int32_t *q_lengths, int32_t nq, int32_t max_lq, const void *docs, int64_t stride,
                  const int32_t *offsets, const int32_t *lengths, const int32_t *doc_query, int32_t B,
-                 float *scores, void *stream_ptr)
+                 float doc_scale, float *scores, void *stream_ptr)
 {
     QueryTable qt;
     int st = check_queries(q_offsets, q_lengths, nq, q_rows, max_lq, doc_query, B, &qt);
     if (st != MAXSIM_OK) return st;
     st = check_common(Qs, max_lq, d, docs, stride, offsets, lengths, B, scores);
     if (st != MAXSIM_OK) return st;
+    if ((fmt & kFmtFp8Docs) && (st = check_fp8(d, stride, doc_scale)) != MAXSIM_OK) return st;
     if (B == 0) return MAXSIM_OK;
-    return run_all(dtype, Qs, qt, d, docs, stride, offsets, lengths, B, scores, 1.0f,
+    return run_all(fmt, Qs, qt, d, docs, stride, offsets, lengths, B, scores, doc_scale,
                    static_cast<hipStream_t>(stream_ptr));
 }
 
@@ -704,9 +709,9 @@ int rerank_pairs(int dtype, const void *Qs, int32_t q_rows, int32_t d, const int
 // tiles, each query starting on a tile; a query longer than a group has a pass of its
 // own. One plan serves every pass; each pass is one score launch and one combine
 // launch, reading the docs once for all of its queries. Empty queries score 0.
-int rerank_multi(int dtype, const void *Qs, const int32_t *q_lengths, int32_t nq, int32_t d,
+int rerank_multi(int fmt, const void *Qs, const int32_t *q_lengths, int32_t nq, int32_t d,
                  const void *docs, int64_t stride, const int32_t *offsets, const int32_t *lengths,
-                 int32_t B, float *scores, void *stream_ptr)
+                 int32_t B, float doc_scale, float *scores, void *stream_ptr)
 {
     if (nq < 0 || (nq > 0 && !q_lengths)) return MAXSIM_ERR_INVALID_ARG;
     int64_t total_rows = 0;
@@ -715,8 +720,9 @@ int rerank_multi(int dtype, const void *Qs, const int32_t *q_lengths, int32_t nq
         if (q_lengths[j] > kMaxLq) return MAXSIM_ERR_UNSUPPORTED;
         total_rows += q_lengths[j];
     }
-    const int st = check_common(Qs, total_rows > 0 ? 1 : 0, d, docs, stride, offsets, lengths, B, scores, nq > 0);
+    int st = check_common(Qs, total_rows > 0 ? 1 : 0, d, docs, stride, offsets, lengths, B, scores, nq > 0);
     if (st != MAXSIM_OK) return st;
+    if ((fmt & kFmtFp8Docs) && (st = check_fp8(d, stride, doc_scale)) != MAXSIM_OK) return st;
     if (B == 0 || nq == 0) return MAXSIM_OK;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
 
@@ -794,8 +800,8 @@ int rerank_multi(int dtype, const void *Qs, const int32_t *q_lengths, int32_t nq
         const void *Qp = qbytes + (size_t)ps.row0 * (size_t)d * 2;
         float *sp = scores + (size_t)ps.j0 * (size_t)B;
         const int rows = ps.tiles * kTileRows;
-        rc = launch_score(dtype, Qp, rows, d, docs, stride, sp, L, w, qt, 1.0f, stream);
-        if (rc == MAXSIM_OK) rc = launch_finish(dtype, rows, d, sp, L, w, qt, 1.0f, stream);
+        rc = launch_score(fmt, Qp, rows, d, docs, stride, sp, L, w, qt, doc_scale, stream);
+        if (rc == MAXSIM_OK) rc = launch_finish(fmt, rows, d, sp, L, w, qt, doc_scale, stream);
     }
     if (hipFreeAsync(ws, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
     return rc;
@@ -857,7 +863,7 @@ int maxsim_rerank_pairs(const void *Qs, int32_t q_rows, int32_t d, const int32_t
                         const int32_t *doc_query, int32_t B, float *scores, void *stream)
 {
     return rerank_pairs(MAXSIM_F16, Qs, q_rows, d, q_offsets, q_lengths, nq, max_lq, docs, stride,
-                        doc_offsets, doc_lengths, doc_query, B, scores, stream);
+                        doc_offsets, doc_lengths, doc_query, B, 1.0f, scores, stream);
 }
 
 int maxsim_rerank_pairs_bf16(const void *Qs, int32_t q_rows, int32_t d, const int32_t *q_offsets,
@@ -866,23 +872,23 @@ int maxsim_rerank_pairs_bf16(const void *Qs, int32_t q_rows, int32_t d, const in
                              const int32_t *doc_query, int32_t B, float *scores, void *stream)
 {
     return rerank_pairs(MAXSIM_BF16, Qs, q_rows, d, q_offsets, q_lengths, nq, max_lq, docs, stride,
-                        doc_offsets, doc_lengths, doc_query, B, scores, stream);
+                        doc_offsets, doc_lengths, doc_query, B, 1.0f, scores, stream);
 }
 
 int maxsim_rerank_multi(const void *Qs, const int32_t *q_lengths, int32_t nq, int32_t d, const void *docs,
                         int64_t stride, const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
                         float *scores, void *stream)
 {
-    return rerank_multi(MAXSIM_F16, Qs, q_lengths, nq, d, docs, stride, doc_offsets, doc_lengths, B, scores,
-                        stream);
+    return rerank_multi(MAXSIM_F16, Qs, q_lengths, nq, d, docs, stride, doc_offsets, doc_lengths, B, 1.0f,
+                        scores, stream);
 }
 
 int maxsim_rerank_multi_bf16(const void *Qs, const int32_t *q_lengths, int32_t nq, int32_t d,
                              const void *docs, int64_t stride, const int32_t *doc_offsets,
                              const int32_t *doc_lengths, int32_t B, float *scores, void *stream)
 {
-    return rerank_multi(MAXSIM_BF16, Qs, q_lengths, nq, d, docs, stride, doc_offsets, doc_lengths, B, scores,
-                        stream);
+    return rerank_multi(MAXSIM_BF16, Qs, q_lengths, nq, d, docs, stride, doc_offsets, doc_lengths, B, 1.0f,
+                        scores, stream);
 }
 
 int maxsim_rerank_fp8(const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
@@ -914,6 +920,25 @@ int maxsim_rerank_topk_bf16(const void *Q, int32_t Lq, int32_t d, const void *do
 {
     return rerank_topk(MAXSIM_BF16, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, k, top_scores, top_ids,
                        stream);
+}
+
+int maxsim_rerank_pairs_fp8(int dtype, const void *Qs, int32_t q_rows, int32_t d, const int32_t *q_offsets,
+                            const int32_t *q_lengths, int32_t nq, int32_t max_lq, const void *docs,
+                            int64_t stride, const int32_t *doc_offsets, const int32_t *doc_lengths,
+                            const int32_t *doc_query, int32_t B, float doc_scale, float *scores, void *stream)
+{
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
+    return rerank_pairs(dtype | kFmtFp8Docs, Qs, q_rows, d, q_offsets, q_lengths, nq, max_lq, docs, stride,
+                        doc_offsets, doc_lengths, doc_query, B, doc_scale, scores, stream);
+}
+
+int maxsim_rerank_multi_fp8(int dtype, const void *Qs, const int32_t *q_lengths, int32_t nq, int32_t d,
+                            const void *docs, int64_t stride, const int32_t *doc_offsets,
+                            const int32_t *doc_lengths, int32_t B, float doc_scale, float *scores, void *stream)
+{
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
+    return rerank_multi(dtype | kFmtFp8Docs, Qs, q_lengths, nq, d, docs, stride, doc_offsets, doc_lengths, B,
+                        doc_scale, scores, stream);
 }
 
 const char *maxsim_status_string(int status)

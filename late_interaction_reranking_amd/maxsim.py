@@ -28,6 +28,9 @@ The functions carry the C ABI's names (include/maxsim.h) and take torch tensors:
                        FP8 E4M3 docs (uint8 or float8_e4m3fn), fp16 or bf16 Q
     maxsim_score_fp8(...), maxsim_finish_fp8(...)   staged form, after maxsim_plan
 
+    maxsim_rerank_pairs_fp8(Qs, ..., doc_query, doc_scale)      pairs over FP8 docs
+    maxsim_rerank_multi_fp8(Qs, q_lengths, docs8, ..., doc_scale) shared docs, FP8
+
     maxsim_topk(scores, k) -> (top_scores [k], top_ids [k])   device top-k
     maxsim_rerank_topk(Q, docs, doc_offsets, doc_lengths, k)  scores + top-k, one call
 
@@ -71,6 +74,8 @@ __all__ = [
     "maxsim_finish_fp8",
     "maxsim_topk",
     "maxsim_rerank_topk",
+    "maxsim_rerank_pairs_fp8",
+    "maxsim_rerank_multi_fp8",
     "MAXSIM_F16",
     "MAXSIM_BF16",
 ]
@@ -141,6 +146,11 @@ def load() -> ctypes.CDLL:
         lib.maxsim_score_fp8.argtypes = [ctypes.c_int, P, I32, I32, P, I64, P, P, I32, F32, P, P, SZ, P]
         lib.maxsim_finish_fp8.restype = ctypes.c_int
         lib.maxsim_finish_fp8.argtypes = [ctypes.c_int, I32, I32, I32, F32, P, P, SZ, P]
+        lib.maxsim_rerank_pairs_fp8.restype = ctypes.c_int
+        lib.maxsim_rerank_pairs_fp8.argtypes = [ctypes.c_int, P, I32, I32, P, P, I32, I32, P, I64, P, P, P, I32,
+                                                F32, P, P]
+        lib.maxsim_rerank_multi_fp8.restype = ctypes.c_int
+        lib.maxsim_rerank_multi_fp8.argtypes = [ctypes.c_int, P, P, I32, I32, P, I64, P, P, I32, F32, P, P]
         lib.maxsim_topk_workspace_size.restype = ctypes.c_int
         lib.maxsim_topk_workspace_size.argtypes = [I32, I32, ctypes.POINTER(SZ)]
         lib.maxsim_topk.restype = ctypes.c_int
@@ -523,3 +533,46 @@ def maxsim_rerank_topk(Q, docs, doc_offsets, doc_lengths, k: int):
                                    _stream(docs))
     _check(st, name)
     return top_scores, top_ids
+
+
+def maxsim_rerank_pairs_fp8(Qs, q_offsets, q_lengths, max_lq: int, docs, doc_offsets, doc_lengths, doc_query,
+                            doc_scale: float, scores=None) -> torch.Tensor:
+    """maxsim_rerank_pairs over docs stored as FP8 E4M3 bytes (element = doc_scale *
+    e4m3); Qs fp16 or bf16."""
+    _, d, stride, B = _check_fp8_args(Qs, docs, doc_offsets, doc_lengths)
+    dev = docs.device
+    for name, t in (("q_offsets", q_offsets), ("q_lengths", q_lengths), ("doc_query", doc_query)):
+        _int32_vec(t, name, dev)
+    if q_offsets.shape != q_lengths.shape or doc_query.shape[0] != B:
+        raise ValueError("q_offsets / q_lengths: one entry per query; doc_query: one per doc")
+    if scores is None:
+        scores = torch.empty(B, dtype=torch.float32, device=dev)
+    code = MAXSIM_BF16 if Qs.dtype == torch.bfloat16 else MAXSIM_F16
+    with torch.cuda.device(dev):
+        st = load().maxsim_rerank_pairs_fp8(
+            code, Qs.data_ptr(), int(Qs.shape[0]), d, q_offsets.data_ptr(), q_lengths.data_ptr(),
+            int(q_offsets.shape[0]), int(max_lq), docs.data_ptr(), stride, doc_offsets.data_ptr(),
+            doc_lengths.data_ptr(), doc_query.data_ptr(), B, float(doc_scale), scores.data_ptr(), _stream(docs))
+    _check(st, "maxsim_rerank_pairs_fp8")
+    return scores
+
+
+def maxsim_rerank_multi_fp8(Qs, q_lengths, docs, doc_offsets, doc_lengths, doc_scale: float,
+                            scores=None) -> torch.Tensor:
+    """maxsim_rerank_multi over docs stored as FP8 E4M3 bytes (element = doc_scale *
+    e4m3); Qs fp16 or bf16; q_lengths a host sequence. Returns [nq, B]."""
+    _, d, stride, B = _check_fp8_args(Qs, docs, doc_offsets, doc_lengths)
+    ql = [int(x) for x in (q_lengths.tolist() if hasattr(q_lengths, "tolist") else q_lengths)]
+    nq = len(ql)
+    if sum(ql) != Qs.shape[0]:
+        raise ValueError("Qs must hold exactly the rows of the queries, back to back")
+    host = (ctypes.c_int32 * max(nq, 1))(*ql)
+    if scores is None:
+        scores = torch.empty((nq, B), dtype=torch.float32, device=docs.device)
+    code = MAXSIM_BF16 if Qs.dtype == torch.bfloat16 else MAXSIM_F16
+    with torch.cuda.device(docs.device):
+        st = load().maxsim_rerank_multi_fp8(code, Qs.data_ptr(), ctypes.cast(host, ctypes.c_void_p), nq, d,
+                                            docs.data_ptr(), stride, doc_offsets.data_ptr(), doc_lengths.data_ptr(),
+                                            B, float(doc_scale), scores.data_ptr(), _stream(docs))
+    _check(st, "maxsim_rerank_multi_fp8")
+    return scores

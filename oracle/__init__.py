@@ -206,13 +206,14 @@ def maxsim_fp8(qfmt, Q, X8, offsets, lengths, doc_scale, d=None, threads: int = 
 
 
 def maxsim_pairs(fmt, Qs, q_offsets, q_lengths, X, offsets, lengths, doc_query, max_lq,
-                 d=None, threads: int = 0) -> np.ndarray:
+                 d=None, threads: int = 0, X8=None, doc_scale: float = 1.0) -> np.ndarray:
     """fp64 scores of docs that each take their own query.
 
     Query j is rows [q_offsets[j], q_offsets[j] + q_lengths[j]) of Qs (uint16 bits,
     [q_rows, d]); doc i is scored, as by ``maxsim``, against query doc_query[i]. A doc
     gets NaN when its query index is outside [0, nq) or that query has a negative
-    offset or length, more than max_lq rows, or rows past the end of Qs.
+    offset or length, more than max_lq rows, or rows past the end of Qs. With X8 (FP8
+    E4M3 bytes) the docs are X8 with doc_scale, as by ``maxsim_fp8``, and X is unused.
     """
     Qs = np.ascontiguousarray(Qs, dtype=np.uint16)
     d = Qs.shape[1] if d is None else int(d)
@@ -230,19 +231,27 @@ def maxsim_pairs(fmt, Qs, q_offsets, q_lengths, X, offsets, lengths, doc_query, 
         if lo < 0 or n < 0 or n > max_lq or lo + n > q_rows:
             continue
         sel = np.nonzero(doc_query == j)[0]
-        out[sel] = maxsim(fmt, Qs[lo:lo + n], X, offsets[sel], lengths[sel], d=d, threads=threads)
+        if X8 is not None:
+            out[sel] = maxsim_fp8(fmt, Qs[lo:lo + n], X8, offsets[sel], lengths[sel], doc_scale, d=d,
+                                  threads=threads)
+        else:
+            out[sel] = maxsim(fmt, Qs[lo:lo + n], X, offsets[sel], lengths[sel], d=d, threads=threads)
     return out
 
 
-def maxsim_multi(fmt, Qs, q_lengths, X, offsets, lengths, d=None, threads: int = 0) -> np.ndarray:
+def maxsim_multi(fmt, Qs, q_lengths, X, offsets, lengths, d=None, threads: int = 0, X8=None,
+                 doc_scale: float = 1.0) -> np.ndarray:
     """fp64 scores [nq, B]: query j (rows sum(q_lengths[:j]) .. + q_lengths[j] - 1 of
-    Qs) against every doc, as by ``maxsim``."""
+    Qs) against every doc, as by ``maxsim`` (or ``maxsim_fp8`` with X8, doc_scale)."""
     Qs = np.ascontiguousarray(Qs, dtype=np.uint16)
     q_lengths = np.asarray(q_lengths, np.int64)
     out = np.empty((q_lengths.shape[0], np.asarray(offsets).shape[0]), np.float64)
     lo = 0
     for j, n in enumerate(q_lengths.tolist()):
-        out[j] = maxsim(fmt, Qs[lo:lo + n], X, offsets, lengths, d=d, threads=threads)
+        if X8 is not None:
+            out[j] = maxsim_fp8(fmt, Qs[lo:lo + n], X8, offsets, lengths, doc_scale, d=d, threads=threads)
+        else:
+            out[j] = maxsim(fmt, Qs[lo:lo + n], X, offsets, lengths, d=d, threads=threads)
         lo += n
     return out
 
@@ -256,13 +265,14 @@ def maxsim_workload(w, docs=None, threads: int = 0) -> np.ndarray:
         docs = np.asarray(docs, dtype=np.int64)
         offs, lens = offs[docs], lens[docs]
         dq = None if dq is None else dq[docs]
-    if w.X8 is not None:
-        return maxsim_fp8(w.dtype, w.Q, w.X8, offs, lens, w.doc_scale, d=w.d, threads=threads)
     if w.q_lengths is not None and dq is None:
-        return maxsim_multi(w.dtype, w.Q, w.q_lengths, w.X, offs, lens, d=w.d, threads=threads)
+        return maxsim_multi(w.dtype, w.Q, w.q_lengths, w.X, offs, lens, d=w.d, threads=threads, X8=w.X8,
+                            doc_scale=w.doc_scale)
     if dq is not None:
         return maxsim_pairs(w.dtype, w.Q, w.q_offsets, w.q_lengths, w.X, offs, lens, dq, w.Lq,
-                            d=w.d, threads=threads)
+                            d=w.d, threads=threads, X8=w.X8, doc_scale=w.doc_scale)
+    if w.X8 is not None:
+        return maxsim_fp8(w.dtype, w.Q, w.X8, offs, lens, w.doc_scale, d=w.d, threads=threads)
     return maxsim(w.dtype, w.Q, w.X, offs, lens, d=w.d, threads=threads)
 
 

@@ -35,7 +35,8 @@ def test_header_declares_the_boundary():
               "maxsim_version", "maxsim_rerank_pairs", "maxsim_rerank_pairs_bf16",
               "maxsim_plan_pairs", "maxsim_rerank_multi", "maxsim_rerank_multi_bf16",
               "maxsim_rerank_fp8", "maxsim_rerank_fp8_bf16", "maxsim_score_fp8", "maxsim_finish_fp8",
-              "maxsim_topk_workspace_size", "maxsim_topk", "maxsim_rerank_topk", "maxsim_rerank_topk_bf16"):
+              "maxsim_topk_workspace_size", "maxsim_topk", "maxsim_rerank_topk", "maxsim_rerank_topk_bf16",
+              "maxsim_rerank_pairs_fp8", "maxsim_rerank_multi_fp8"):
         assert n in names
 
 
@@ -267,3 +268,30 @@ def test_rerank_topk_validation(lib, fn):
     assert rt(docs=None) == INVALID
     assert rt(B=-1) == INVALID
     assert rt(k=0, ts=None, ti=None) == OK
+
+
+def test_fp8_batch_forms_validation(lib):
+    f = ctypes.c_float
+    ql = (ctypes.c_int32 * 2)(32, 16)
+    qp = ctypes.cast(ql, ctypes.c_void_p)
+
+    def multi(dtype=0, d=128, stride=128, scale=0.5, B=10, docs=FAKE):
+        return lib.maxsim_rerank_multi_fp8(dtype, FAKE, qp, 2, d, docs, stride, FAKE, FAKE + 1024, B, f(scale),
+                                           FAKE + 4096, None)
+
+    assert multi(dtype=2) == INVALID
+    assert multi(scale=0.0) == INVALID
+    assert multi(d=120, stride=128) == UNSUPPORTED
+    assert multi(stride=136) == UNSUPPORTED
+    assert multi(docs=None) == INVALID
+    assert multi(B=0) == OK
+
+    def pairs(dtype=1, d=128, stride=128, scale=0.5, B=10, max_lq=32):
+        return lib.maxsim_rerank_pairs_fp8(dtype, FAKE, 64, d, FAKE + 8192, FAKE + 12288, 4, max_lq, FAKE, stride,
+                                           FAKE, FAKE + 1024, FAKE + 16384, B, f(scale), FAKE + 4096, None)
+
+    assert pairs(dtype=-1) == INVALID
+    assert pairs(scale=float("inf")) == INVALID
+    assert pairs(d=48, stride=56) == UNSUPPORTED
+    assert pairs(max_lq=300) == UNSUPPORTED
+    assert pairs(B=0) == OK

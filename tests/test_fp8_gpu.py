@@ -155,3 +155,58 @@ def test_fp8_large_sampled():
     rng = np.random.default_rng(0)
     sample = np.unique(np.concatenate([w.planted, rng.choice(w.B, 3000, replace=False), [0, w.B - 1]]))
     assert_parity(got[sample], oracle.maxsim_workload(w, docs=sample), "large_fp8 (sample)")
+
+
+# ------------------------------------------------------------------ batch forms
+
+
+def _i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(DEV)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_fp8_pairs_batch(fmt):
+    _say(f"[fp8] pairs {fmt}")
+    rng = np.random.default_rng(31)
+    q_lengths = rng.integers(0, 65, size=9)
+    q_lengths[:2] = [0, 64]
+    per = rng.integers(0, 30, size=9)
+    lengths = rng.integers(0, 300, size=int(per.sum()))
+    lengths[rng.choice(lengths.size, 3, replace=False)] = [3000, 4500, 6000]
+    w = workloads.custom_pairs(q_lengths, 96, per, lengths, dtype=fmt, seed=31, interleave=True,
+                               order="shuffled", gap=(0, 4), gap_fill="nan")
+    workloads.to_fp8(w, doc_scale=0.02)
+    Q, X8, offs, lens = upload8(w)
+    got = lir.maxsim_rerank_pairs_fp8(Q, _i32(w.q_offsets), _i32(w.q_lengths), w.Lq, X8, offs, lens,
+                                      _i32(w.doc_query), w.doc_scale).cpu().numpy().astype(np.float64)
+    ref = oracle.maxsim_workload(w)
+    assert_parity(got, ref, f"fp8 pairs {fmt}")
+    for j in range(w.nq):  # each doc equals its query scored alone
+        sel = np.nonzero(w.doc_query == j)[0]
+        if not sel.size:
+            continue
+        lo, n = int(w.q_offsets[j]), int(w.q_lengths[j])
+        Qj = Q[lo:lo + n].contiguous()
+        alone = lir.maxsim_rerank_fp8(Qj, X8, offs[sel].contiguous(), lens[sel].contiguous(), w.doc_scale)
+        assert np.array_equal(got[sel], alone.cpu().numpy().astype(np.float64)), j
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_fp8_shared_docs(fmt):
+    _say(f"[fp8] shared docs {fmt}")
+    rng = np.random.default_rng(32)
+    q_lengths = [32, 0, 17, 32, 100, 5, 32]
+    lengths = rng.integers(0, 300, size=150)
+    lengths[:3] = [0, 5000, 1]
+    w = workloads.custom_multi(q_lengths, 128, lengths, dtype=fmt, seed=32, order="shuffled", gap=(0, 3),
+                               gap_fill="nan")
+    workloads.to_fp8(w, doc_scale=1 / 128)
+    Q, X8, offs, lens = upload8(w)
+    got = lir.maxsim_rerank_multi_fp8(Q, w.q_lengths, X8, offs, lens, w.doc_scale).cpu().numpy().astype(np.float64)
+    ref = oracle.maxsim_workload(w)
+    lo = 0
+    for j, n in enumerate(q_lengths):
+        assert_parity(got[j], ref[j], f"fp8 shared query {j}")
+        alone = lir.maxsim_rerank_fp8(Q[lo:lo + n].contiguous(), X8, offs, lens, w.doc_scale)
+        assert np.array_equal(got[j], alone.cpu().numpy().astype(np.float64)), j
+        lo += n

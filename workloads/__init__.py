@@ -43,6 +43,7 @@ __all__ = [
     "shared",
     "custom_multi",
     "large_fp8",
+    "shared_fp8",
     "to_fp8",
     "E4M3_NAN",
     "round_f16",
@@ -448,6 +449,14 @@ def large_fp8(seed: int = 4, **kw) -> Workload:
     return to_fp8(w, keep_x=False)
 
 
+def shared_fp8(seed: int = 6, **kw) -> Workload:
+    """The shared workload (8 queries of 32 rows, the same 80,000 docs) with docs stored
+    as FP8 E4M3 bytes, doc scale 2^-8, rows 128 bytes apart (~2.6 GB)."""
+    w = shared(seed=seed, **kw)
+    w.name = "shared_fp8"
+    return to_fp8(w, keep_x=False)
+
+
 def custom_multi(q_lengths, d: int, doc_lengths, *, dtype: str = "f16", seed: int = 0,
                  name: str = "custom_multi", **kw) -> Workload:
     """Several queries (rows back to back in Q, lengths q_lengths) that all score the
@@ -482,6 +491,7 @@ CONFIGS = {
     "pairs": pairs,
     "shared": shared,
     "large_fp8": large_fp8,
+    "shared_fp8": shared_fp8,
 }
 
 
