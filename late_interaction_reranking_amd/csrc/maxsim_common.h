@@ -94,15 +94,25 @@ inline Layout make_layout(int lq_pad, int32_t B, uint32_t waves_max)
 // The query rows of one score launch as 16-row query tiles: the one query of a
 // single-query launch, or several queries that score the same docs, each starting on
 // a tile boundary (a tile never mixes two queries, so each query's rows meet the lanes
-// exactly as they would alone). Tile T holds rows src[T] .. src[T] + rows[T] - 1 of Q;
-// ends[T] >= 0 says that tile T is its query's last and gives that query's score row
-// (scores + ends[T] * score_stride). Not used under a multi-query "pairs" plan, whose
+// exactly as they would alone). Tile T holds rows src(T) .. src(T) + rows(T) - 1 of Q;
+// end(T) >= 0 says that tile T is its query's last and gives that query's score row
+// (scores + end(T) * score_stride). Not used under a multi-query "pairs" plan, whose
 // docs carry their own query rows.
+// One 32-bit word per tile, so that a kernel reads an entry at a wave-uniform index with
+// one scalar load (narrower fields would need vector loads, whose waits also wait for
+// the doc tiles already in flight).
 struct QueryTiles {
     int64_t score_stride;           // elements between the score rows of two queries
-    uint16_t src[kMaxQTiles];
-    uint8_t rows[kMaxQTiles];       // 0 .. 16
-    int8_t ends[kMaxQTiles];        // score row completed by tile T, or -1
+    uint32_t tile[kMaxQTiles];      // src (bits 0-15), rows 0..16 (16-23), end as int8 (24-31)
+
+    __host__ __device__ int src(int T) const { return (int)(tile[T] & 0xFFFFu); }
+    __host__ __device__ int rows(int T) const { return (int)((tile[T] >> 16) & 0xFFu); }
+    __host__ __device__ int end(int T) const { return (int)(int8_t)(uint8_t)(tile[T] >> 24); }
+    __host__ __device__ void set(int T, int src_row, int nrows, int end_row)
+    {
+        tile[T] = (uint32_t)(src_row & 0xFFFF) | ((uint32_t)(nrows & 0xFF) << 16) |
+                  ((uint32_t)(uint8_t)(int8_t)end_row << 24);
+    }
 };
 
 struct ScoreArgs {

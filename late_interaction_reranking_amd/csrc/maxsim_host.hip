@@ -284,8 +284,8 @@ combine_kernel(const CombineArgs a)
                     nr = left < 0 ? 0 : (left > kTileRows ? kTileRows : left);
                     end = T == ntiles - 1 ? 0 : -1;
                 } else {
-                    nr = a.qt.rows[T];
-                    end = a.qt.ends[T];
+                    nr = a.qt.rows(T);
+                    end = a.qt.end(T);
                 }
                 for (int i = 0; i < 4; ++i)
                     lane_sum += kgroup * 4 + i < nr ? s_part[0][T * kTileRows + kgroup * 4 + i] : 0.0f;
@@ -512,9 +512,8 @@ QueryTiles single_tiles(int32_t Lq)
     const int nt = (Lq + kTileRows - 1) / kTileRows;
     for (int T = 0; T < kMaxQTiles; ++T) {
         const int left = Lq - T * kTileRows;
-        t.src[T] = (uint16_t)(T < nt ? T * kTileRows : 0);
-        t.rows[T] = (uint8_t)(left <= 0 ? 0 : (left > kTileRows ? kTileRows : left));
-        t.ends[T] = (int8_t)(T == nt - 1 ? 0 : -1);
+        t.set(T, T < nt ? T * kTileRows : 0, left <= 0 ? 0 : (left > kTileRows ? kTileRows : left),
+              T == nt - 1 ? 0 : -1);
     }
     return t;
 }
@@ -783,7 +782,7 @@ int rerank_multi(int fmt, const void *Qs, const int32_t *q_lengths, int32_t nq, 
         const Pass &ps = passes[p];
         QueryTiles qt{};
         qt.score_stride = B;
-        for (int T = 0; T < kMaxQTiles; ++T) qt.ends[T] = -1;
+        for (int T = 0; T < kMaxQTiles; ++T) qt.set(T, 0, 0, -1);
         int T = 0;
         int64_t rel = 0;  // row of query j relative to the pass
         for (int32_t j = ps.j0; j < ps.j1; ++j) {
@@ -791,9 +790,8 @@ int rerank_multi(int fmt, const void *Qs, const int32_t *q_lengths, int32_t nq, 
             const int t = (Lj + kTileRows - 1) / kTileRows;
             for (int k = 0; k < t; ++k, ++T) {
                 const int left = Lj - k * kTileRows;
-                qt.src[T] = (uint16_t)(rel + k * kTileRows);
-                qt.rows[T] = (uint8_t)(left > kTileRows ? kTileRows : left);
-                qt.ends[T] = (int8_t)(k == t - 1 ? j - ps.j0 : -1);
+                qt.set(T, (int)(rel + k * kTileRows), left > kTileRows ? kTileRows : left,
+                       k == t - 1 ? j - ps.j0 : -1);
             }
             rel += Lj;
         }

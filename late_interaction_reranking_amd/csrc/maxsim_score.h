@@ -81,6 +81,9 @@ constexpr int kBufferWord3 = 0x00020000;
 // exactly once; with the default policy the same stream runs ~12 % slower on MI355X
 // (6.2 vs 6.9 TB/s measured for plain 1 KB-per-instruction reads).
 constexpr int kDocLoadPolicy = 2;
+// s_waitcnt operand (gfx9 encoding) that waits for every vector memory load of the
+// wave: vmcnt 0, expcnt and lgkmcnt at their maxima (no wait on them).
+constexpr int kWaitAllVmem = 0x0F70;
 
 template <bool BF16>
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c)
@@ -111,6 +114,27 @@ __device__ __forceinline__ float row16_max(float v)
     v = fmax_plain(v, dpp_move<0x122>(v));
     v = fmax_plain(v, dpp_move<0x121>(v));
     return v;
+}
+
+// The doc descriptors, written by the plan kernels before the score launch, are
+// read-only while it runs: read through the constant address space, a descriptor at a
+// wave-uniform index comes in one scalar load, whose wait leaves the vector loads of the
+// doc tiles in flight alone.
+typedef __attribute__((address_space(4))) const DocDesc ConstDocDesc;
+
+__device__ __forceinline__ DocDesc load_desc(const DocDesc *desc, uint32_t i)
+{
+    ConstDocDesc *c = (ConstDocDesc *)desc + i;
+    DocDesc d;
+    d.doc = c->doc;
+    d.offset = c->offset;
+    d.length = c->length;
+    d.tiles = c->tiles;
+    d.query = c->query;
+    d.q_offset = c->q_offset;
+    d.q_length = c->q_length;
+    d.reserved = c->reserved;
+    return d;
 }
 
 __device__ __forceinline__ uint32_t wave_uniform(uint32_t v)
@@ -179,8 +203,8 @@ score_kernel(const ScoreArgs a)
             const int T = r / kTileRows;
             const int ri = r - T * kTileRows;
             u32x4 v = {0u, 0u, 0u, 0u};
-            if (ri < (int)a.qt.rows[T] && c * 8 < a.d)
-                v = *reinterpret_cast<const u32x4 *>(a.Q + ((size_t)a.qt.src[T] + ri) * a.d + c * 8);
+            if (ri < a.qt.rows(T) && c * 8 < a.d)
+                v = *reinterpret_cast<const u32x4 *>(a.Q + ((size_t)a.qt.src(T) + ri) * a.d + c * 8);
             *reinterpret_cast<u32x4 *>(qs + r * LDQ + c * 8) = v;
         }
     }
@@ -222,23 +246,34 @@ score_kernel(const ScoreArgs a)
     // item's query at rows [q_off, q_off + q_len) of Q.
     u32x4 qf[NQT][NKS];
     auto load_q = [&](int grp, int q_off, int q_len) {
+        if (stage_q) {
 #pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-            const int T = grp * NQT + qt;
-            const int row = T * kTileRows + row_in_tile;
-            const bool row_ok = pairs ? row < q_len : row_in_tile < (int)a.qt.rows[T];
-            const size_t src = pairs ? (size_t)q_off + row : (size_t)a.qt.src[T] + row_in_tile;
+            for (int qt = 0; qt < NQT; ++qt) {
+                const int row = (grp * NQT + qt) * kTileRows + row_in_tile;
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) {
-                const int col = (s * 4 + kgroup) * 8;
-                if (stage_q) {
-                    qf[qt][s] = *reinterpret_cast<const u32x4 *>(qs + row * LDQ + col);
-                } else {
+                for (int s = 0; s < NKS; ++s)
+                    qf[qt][s] = *reinterpret_cast<const u32x4 *>(qs + row * LDQ + (s * 4 + kgroup) * 8);
+            }
+        } else {
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                const int T = grp * NQT + qt;
+                const int row = T * kTileRows + row_in_tile;
+                const bool row_ok = pairs ? row < q_len : row_in_tile < a.qt.rows(T);
+                const size_t src = pairs ? (size_t)q_off + row : (size_t)a.qt.src(T) + row_in_tile;
+#pragma unroll
+                for (int s = 0; s < NKS; ++s) {
+                    const int col = (s * 4 + kgroup) * 8;
                     u32x4 v = {0u, 0u, 0u, 0u};
                     if (row_ok && col < a.d) v = *reinterpret_cast<const u32x4 *>(a.Q + src * a.d + col);
                     qf[qt][s] = v;
                 }
             }
+            // The fragments are waited for here, on this path alone. Otherwise the
+            // compiler's wait-count analysis, which cannot tell the two paths apart where
+            // they meet at the tile loop, makes every pass of that loop wait for all of
+            // the wave's loads in flight, its prefetched doc tiles too.
+            __builtin_amdgcn_s_waitcnt(kWaitAllVmem);
         }
     };
     int loaded_query = -1;  // query whose fragments qf holds (one register group only)
@@ -263,7 +298,7 @@ score_kernel(const ScoreArgs a)
     auto fetch = [&](uint32_t g, Item &it, DocDesc &dd) {
         if (g < total) {
             it = locate_claim(L, lane, g);
-            dd = a.desc[it.di];
+            dd = load_desc(a.desc, it.di);
         }
     };
     auto resolve = [&](uint32_t g, const Item &it, const DocDesc &dd) -> Span {
@@ -428,8 +463,8 @@ score_kernel(const ScoreArgs a)
                     nr = left < 0 ? 0 : (left > kTileRows ? kTileRows : left);
                     end = T == ngroups * NQT - 1 ? 0 : -1;
                 } else {
-                    nr = a.qt.rows[T];
-                    end = a.qt.ends[T];
+                    nr = a.qt.rows(T);
+                    end = a.qt.end(T);
                 }
 #pragma unroll
                 for (int i = 0; i < 4; ++i) lane_sum += kgroup * 4 + i < nr ? rmax[qt][i] : 0.0f;
