@@ -223,88 +223,168 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
 
 // Split docs: max over each doc's chunk slots, then the score kernel's fixed-order sum
 // (lane l adds, per query tile, rows 4 (l / 16) + 0..3; then lanes 0, 16, 32, 48), so a
-// split doc's score is bitwise the one it would get unsplit. One workgroup per split
-// doc: wave w scans slots w, w + 4, ... with 8 independent loads in flight per lane,
-// the four waves' maxima meet in LDS, and wave 0 sums.
-__global__ void __launch_bounds__(kScoreBlock)
-combine_kernel(const CombineArgs a)
+// split doc's score is bitwise the one it would get unsplit. The slots are read as cells
+// of 4 consecutive query rows (16 bytes) of one slot, every cell of a doc in one round of
+// independent loads: a doc of at most kSoloCells cells is reduced by one wave, lanes over
+// (row quad, slot), and a larger one by a whole workgroup. Docs sit in descending bin
+// order and a bin's chunk count grows with the bin, so the larger docs come first.
+constexpr int kSoloCells = 8 * kWave;
+constexpr int kMaxQuads = kMaxLqPad / 4;
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 max4(f32x4 a, f32x4 b)
+{
+    f32x4 r;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[i] = a[i] > b[i] ? a[i] : b[i];
+    return r;
+}
+
+__device__ __forceinline__ void wave_lds_sync()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Max over slots k = k0, k0 + step, ... < K of cell `quad` (8 loads in flight).
+__device__ __forceinline__ f32x4 slot_max(const float *base, int lq_pad, int quad, uint32_t k0, uint32_t step,
+                                          uint32_t K)
 {
     constexpr float NEG_INF = -__builtin_huge_valf();
     constexpr int U = 8;
+    f32x4 m = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+    for (uint32_t k = k0; k < K; k += U * step) {
+        f32x4 v[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const uint32_t ku = k + u * step;
+            v[u] = ku < K ? *reinterpret_cast<const f32x4 *>(base + (size_t)ku * lq_pad + quad * 4)
+                          : f32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) m = max4(m, v[u]);
+    }
+    return m;
+}
+
+// One wave: the score kernel's per-query sums of the row maxima in rmax (lq_pad rows as
+// quads), in its order (query tiles ascending, lane groups last), stored as it stores them.
+__device__ __forceinline__ void combine_sums(const CombineArgs &a, const f32x4 *rmax, const DocDesc &dd,
+                                             bool pairs, int lane)
+{
+    const int kgroup = lane >> 4;
+    const int ntiles = a.ngroups * a.nqt;
+    float lane_sum = 0.0f;
+    for (int T = 0; T < ntiles; ++T) {
+        int nr, end;
+        if (pairs) {
+            const int left = dd.q_length - T * kTileRows;
+            nr = left < 0 ? 0 : (left > kTileRows ? kTileRows : left);
+            end = T == ntiles - 1 ? 0 : -1;
+        } else {
+            nr = a.qt.rows(T);
+            end = a.qt.end(T);
+        }
+        const f32x4 m = rmax[T * 4 + kgroup];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lane_sum += kgroup * 4 + i < nr ? m[i] : 0.0f;
+        if (end >= 0) {
+            const int ls = __builtin_bit_cast(int, lane_sum);
+            const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 0));
+            const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 16));
+            const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 32));
+            const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
+            // NaN for an invalid query, chosen and stored as bits (the library is
+            // compiled without NaN semantics for its max steps).
+            const float sum = (((s0 + s1) + s2) + s3) * a.doc_scale;
+            const uint32_t v = pairs && dd.q_length < 0 ? kNaNBits : __builtin_bit_cast(uint32_t, sum);
+            if (lane == 0) reinterpret_cast<uint32_t *>(a.scores)[(size_t)end * a.qt.score_stride + dd.doc] = v;
+            lane_sum = 0.0f;
+        }
+    }
+}
+
+__global__ void __launch_bounds__(kScoreBlock)
+combine_kernel(const CombineArgs a)
+{
     __shared__ BinTables tab;
-    __shared__ float s_part[kScoreWaves][kMaxLqPad];
+    __shared__ f32x4 s_red[kScoreBlock];            // per-thread maxima over its slots
+    __shared__ f32x4 s_quad[kScoreWaves][kMaxQuads];  // a doc's row maxima, per wave
     const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
     if (wave == 0) fill_bin_tables(a.hdr, a.score_waves, tab, lane);
     __syncthreads();
     const LaneBins L = lane_bins(tab, lane);
     const uint32_t split = tab.split_docs;
-    const int kgroup = lane >> 4;
     const int lq_pad = a.lq_pad;
+    const int nquads = lq_pad / 4;
     const bool pairs = a.hdr->multi_query != 0u;
-    for (uint32_t di = blockIdx.x; di < split; di += gridDim.x) {
+    // Workgroup docs: those of the bins whose docs have more than kSoloCells cells; the
+    // lowest such bin b ends at the start of bin b - 1 (bin 0 is never split).
+    const unsigned long long big =
+        __ballot(lane < kNumBins && L.chunks > 1u && (uint64_t)L.chunks * (uint64_t)nquads > kSoloCells);
+    uint32_t coop_end = 0;
+    if (big) {
+        const int b = __builtin_ctzll(big);
+        coop_end = __builtin_amdgcn_readfirstlane(__builtin_amdgcn_readlane(L.desc_start, b - 1));
+    }
+    if (coop_end > split) coop_end = split;
+
+    // Workgroup docs: thread t takes cell t % nquads of the slots t / nquads + j S.
+    const int t = threadIdx.x;
+    for (uint32_t di = blockIdx.x; di < coop_end; di += gridDim.x) {
         const Item it = locate_doc(L, lane, di);
+        const DocDesc dd = load_desc(a.desc, di);
         const float *base = a.partials + (size_t)it.first * lq_pad;
-        for (int q = lane; q < lq_pad; q += kWave) {
-            float m = NEG_INF;
-            uint32_t k = wave;
-            for (; k + (U - 1) * kScoreWaves < it.K; k += U * kScoreWaves) {
-                float v[U];
-#pragma unroll
-                for (int u = 0; u < U; ++u) v[u] = base[(size_t)(k + u * kScoreWaves) * lq_pad + q];
-#pragma unroll
-                for (int u = 0; u < U; ++u) m = v[u] > m ? v[u] : m;
-            }
-            for (; k < it.K; k += kScoreWaves) {
-                const float v = base[(size_t)k * lq_pad + q];
-                m = v > m ? v : m;
-            }
-            s_part[wave][q] = m;
+        const uint32_t S = (uint32_t)(kScoreBlock / nquads);
+        const int quad = t % nquads;
+        const uint32_t sl = (uint32_t)(t / nquads);
+        constexpr float NEG_INF = -__builtin_huge_valf();
+        f32x4 m = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+        if (sl < S) m = slot_max(base, lq_pad, quad, sl, S, it.K);
+        s_red[t] = m;
+        __syncthreads();
+        if (t < nquads) {
+            f32x4 r = s_red[t];
+            for (uint32_t k = 1; k < S; ++k) r = max4(r, s_red[k * nquads + t]);
+            s_quad[0][t] = r;
         }
         __syncthreads();
-        if (wave == 0) {
-            for (int q = lane; q < lq_pad; q += kWave) {
-                float m = s_part[0][q];
-                for (int w = 1; w < kScoreWaves; ++w) m = s_part[w][q] > m ? s_part[w][q] : m;
-                s_part[0][q] = m;
-            }
-            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-            __builtin_amdgcn_wave_barrier();
-            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-            // The score kernel's per-query sums, in its order (query tiles ascending,
-            // lane groups last).
-            const int q_len = a.desc[di].q_length;
-            const int doc = a.desc[di].doc;
-            const int ntiles = a.ngroups * a.nqt;
-            float lane_sum = 0.0f;
-            for (int T = 0; T < ntiles; ++T) {
-                int nr, end;
-                if (pairs) {
-                    const int left = q_len - T * kTileRows;
-                    nr = left < 0 ? 0 : (left > kTileRows ? kTileRows : left);
-                    end = T == ntiles - 1 ? 0 : -1;
-                } else {
-                    nr = a.qt.rows(T);
-                    end = a.qt.end(T);
-                }
-                for (int i = 0; i < 4; ++i)
-                    lane_sum += kgroup * 4 + i < nr ? s_part[0][T * kTileRows + kgroup * 4 + i] : 0.0f;
-                if (end >= 0) {
-                    const int ls = __builtin_bit_cast(int, lane_sum);
-                    const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 0));
-                    const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 16));
-                    const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 32));
-                    const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
-                    // NaN for an invalid query, chosen and stored as bits (the
-                    // library is compiled without NaN semantics for its max steps).
-                    const float sum = (((s0 + s1) + s2) + s3) * a.doc_scale;
-                    const uint32_t v = pairs && q_len < 0 ? kNaNBits : __builtin_bit_cast(uint32_t, sum);
-                    if (lane == 0) reinterpret_cast<uint32_t *>(a.scores)[(size_t)end * a.qt.score_stride + doc] = v;
-                    lane_sum = 0.0f;
-                }
-            }
-        }
+        if (wave == 0) combine_sums(a, s_quad[0], dd, pairs, lane);
         __syncthreads();
+    }
+
+    // One wave per doc: lane l takes cell l % nquads of the slots l / nquads + j S, or,
+    // with more than 64 cells per slot, cells l and l + 64 of every slot.
+    const uint32_t nw = gridDim.x * kScoreWaves;
+    f32x4 *red = s_red + wave * kWave;
+    f32x4 *rq = s_quad[wave];
+    for (uint32_t di = coop_end + blockIdx.x * kScoreWaves + wave; di < split; di += nw) {
+        const Item it = locate_doc(L, lane, di);
+        const DocDesc dd = load_desc(a.desc, di);
+        const float *base = a.partials + (size_t)it.first * lq_pad;
+        if (nquads <= kWave) {
+            const uint32_t S = (uint32_t)(kWave / nquads);
+            const int quad = lane % nquads;
+            const uint32_t sl = (uint32_t)(lane / nquads);
+            constexpr float NEG_INF = -__builtin_huge_valf();
+            f32x4 m = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+            if (sl < S) m = slot_max(base, lq_pad, quad, sl, S, it.K);
+            red[lane] = m;
+            wave_lds_sync();
+            if (lane < nquads) {
+                f32x4 r = red[lane];
+                for (uint32_t k = 1; k < S; ++k) r = max4(r, red[k * nquads + lane]);
+                rq[lane] = r;
+            }
+        } else {
+            rq[lane] = slot_max(base, lq_pad, lane, 0, 1, it.K);
+            if (lane + kWave < nquads) rq[lane + kWave] = slot_max(base, lq_pad, lane + kWave, 0, 1, it.K);
+        }
+        wave_lds_sync();
+        combine_sums(a, rq, dd, pairs, lane);
+        wave_lds_sync();
     }
 }
 
@@ -579,7 +659,7 @@ int launch_finish(int fmt, int32_t Lq, int32_t d, float *scores, const Layout &L
     ca.lq_pad = c.lq_pad;
     ca.qt = qt;
     ca.doc_scale = (fmt & kFmtFp8Docs) ? doc_scale : 1.0f;
-    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)f.cus * 4u), dim3(kScoreBlock), 0, stream, ca);
+    hipLaunchKernelGGL(combine_kernel, dim3((unsigned)f.cus * 8u), dim3(kScoreBlock), 0, stream, ca);
     return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
 }
 

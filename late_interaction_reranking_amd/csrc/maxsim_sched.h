@@ -113,4 +113,25 @@ __device__ inline Item locate_doc(const LaneBins &L, int lane, uint32_t di)
     return it;
 }
 
+// The doc descriptors, written by the plan kernels before the score and combine
+// launches, are read-only while those run: read through the constant address space, a
+// descriptor at a wave-uniform index comes in one scalar load, whose wait leaves the
+// vector loads in flight alone.
+typedef __attribute__((address_space(4))) const DocDesc ConstDocDesc;
+
+__device__ __forceinline__ DocDesc load_desc(const DocDesc *desc, uint32_t i)
+{
+    ConstDocDesc *c = (ConstDocDesc *)desc + i;
+    DocDesc d;
+    d.doc = c->doc;
+    d.offset = c->offset;
+    d.length = c->length;
+    d.tiles = c->tiles;
+    d.query = c->query;
+    d.q_offset = c->q_offset;
+    d.q_length = c->q_length;
+    d.reserved = c->reserved;
+    return d;
+}
+
 }  // namespace maxsim

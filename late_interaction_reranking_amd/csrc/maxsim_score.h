@@ -116,27 +116,6 @@ __device__ __forceinline__ float row16_max(float v)
     return v;
 }
 
-// The doc descriptors, written by the plan kernels before the score launch, are
-// read-only while it runs: read through the constant address space, a descriptor at a
-// wave-uniform index comes in one scalar load, whose wait leaves the vector loads of the
-// doc tiles in flight alone.
-typedef __attribute__((address_space(4))) const DocDesc ConstDocDesc;
-
-__device__ __forceinline__ DocDesc load_desc(const DocDesc *desc, uint32_t i)
-{
-    ConstDocDesc *c = (ConstDocDesc *)desc + i;
-    DocDesc d;
-    d.doc = c->doc;
-    d.offset = c->offset;
-    d.length = c->length;
-    d.tiles = c->tiles;
-    d.query = c->query;
-    d.q_offset = c->q_offset;
-    d.q_length = c->q_length;
-    d.reserved = c->reserved;
-    return d;
-}
-
 __device__ __forceinline__ uint32_t wave_uniform(uint32_t v)
 {
     return __builtin_amdgcn_readfirstlane(v);

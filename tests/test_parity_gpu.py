@@ -88,6 +88,8 @@ SHAPES = [
     (128, 128, 128), (129, 128, 128), (200, 128, 136), (256, 256, 256), (64, 256, 264),
     (33, 8, 8), (20, 40, 48), (45, 200, 208), (7, 160, 160), (100, 32, 32), (200, 200, 200),
     (129, 256, 256),
+    # 18 query tiles in 3 groups (lq_pad 288: more than 64 four-row cells per slot)
+    (256, 160, 160), (250, 136, 136),
 ]
 
 
@@ -104,10 +106,11 @@ def test_shapes_ragged(fmt, Lq, d, stride):
 
 
 @pytest.mark.parametrize("fmt", ["f16", "bf16"])
-def test_long_docs_split_and_tail(fmt):
-    _say(f"[parity] long docs {fmt}")
+@pytest.mark.parametrize("Lq,d", [(64, 128), (256, 160)])
+def test_long_docs_split_and_tail(fmt, Lq, d):
+    _say(f"[parity] long docs Lq={Lq} d={d} {fmt}")
     lengths = np.array([4096, 4095, 1, 2049, 0, 3000, 17, 5000, 16, 8191])
-    w = workloads.custom(64, 128, lengths, dtype=fmt, seed=3, order="shuffled", gap=(1, 3),
+    w = workloads.custom(Lq, d, lengths, dtype=fmt, seed=3, order="shuffled", gap=(1, 3),
                          gap_fill="nan")
     assert_parity(gpu_scores(w), oracle.maxsim_workload(w), "long docs")
 
@@ -196,6 +199,17 @@ def test_chunking_does_not_change_scores():
     b = gpu_scores(many)[0]
     assert a == b
     assert_parity([a], oracle.maxsim_workload(alone), "long doc")
+
+
+def test_combine_mixed_workgroup_and_wave_docs():
+    """Split docs with many chunk slots are combined by a whole workgroup, those with few
+    by one wave: a batch with both (three docs of 6,000-8,000 rows cut into 256 chunks,
+    300 of 65-199 rows cut into 2-8) gets every score within tolerance."""
+    _say("[parity] combine: workgroup and wave docs in one launch")
+    rng = np.random.default_rng(21)
+    lengths = np.concatenate([[8000, 6000, 7777], rng.integers(65, 200, size=300)])
+    w = workloads.custom(64, 128, lengths, seed=21, order="shuffled")
+    assert_parity(gpu_scores(w), oracle.maxsim_workload(w), "mixed combine")
 
 
 def test_query_row_permutation_within_tolerance():
