@@ -134,6 +134,43 @@ struct ScoreArgs {
 // fragments are read from global memory (L2-resident) instead.
 constexpr size_t kMaxQLdsBytes = 64 * 1024;
 
+// ---------------------------------------------------------------- doc-tile pipeline
+// 16-bit docs go from memory straight into LDS (LDS-DMA buffer loads, 16 bytes per
+// lane, no registers in flight). A 16-row tile is kept as rows of dma_row_chunks(NKS)
+// 16-byte chunks: a power of two >= the d / 8 chunks of a row, the rest filled with
+// zeros by out-of-range loads. Each wave owns P such slots. These rules fix an
+// instance's pipeline depth and the occupancy it is built for; the host sizes the
+// kernel's LDS with the same functions.
+constexpr int kLdsPerCu = 160 * 1024;
+constexpr int kScoreStaticLds = 1024;             // bin tables and other static LDS, rounded up
+
+constexpr int dma_row_chunks(int nks) { return nks <= 1 ? 4 : (nks <= 2 ? 8 : (nks <= 4 ? 16 : 32)); }
+constexpr int dma_tile_bytes(int nks) { return kTileRows * dma_row_chunks(nks) * 16; }
+// Registers of one wave: query fragments, one B-fragment set, running maxima,
+// accumulators, addressing and loop state.
+constexpr int dma_regs(int nks, int nqt) { return 4 * nqt * nks + 4 * nks + 4 * nqt + 56; }
+constexpr int dma_waves_per_simd(int nks, int nqt)
+{
+    return dma_regs(nks, nqt) <= 128 ? 4 : (dma_regs(nks, nqt) <= 168 ? 3 : (dma_regs(nks, nqt) <= 256 ? 2 : 1));
+}
+// Workgroups per CU an instance is built for: what its registers allow, at most 3 (four
+// workgroups of LDS-DMA streams per CU read slower than three, measured), and fewer if
+// two tiles in flight per wave would not fit their LDS.
+constexpr int dma_blocks(int nks, int nqt)
+{
+    int b = dma_waves_per_simd(nks, nqt) < 3 ? dma_waves_per_simd(nks, nqt) : 3;
+    while (b > 1 && kScoreWaves * 2 * dma_tile_bytes(nks) > kLdsPerCu / b - kScoreStaticLds) --b;
+    return b;
+}
+// Tiles in flight per wave: up to 16 KB (8 tiles), within a workgroup's share of LDS.
+constexpr int dma_pipe(int nks, int nqt)
+{
+    int p = 16384 / dma_tile_bytes(nks);
+    if (p > 8) p = 8;
+    while (p > 1 && kScoreWaves * p * dma_tile_bytes(nks) > kLdsPerCu / dma_blocks(nks, nqt) - kScoreStaticLds) --p;
+    return p;
+}
+
 // ---------------------------------------------------------------- combine kernel
 struct CombineArgs {
     const Header *hdr;

@@ -447,7 +447,7 @@ int score_blocks_per_cu(const void *fn, size_t lds, int *blocks)
             *blocks = g_occ[i].blocks;
             return MAXSIM_OK;
         }
-    if (lds > 64 * 1024 &&
+    if (lds > 48 * 1024 &&
         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) != hipSuccess)
         return MAXSIM_ERR_HIP;
     int nb = 0;
@@ -489,22 +489,29 @@ bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
 size_t q_lds_bytes(const Config &c) { return (size_t)c.lq_pad * (c.nks * kStepK + 8) * 2; }
 
-// Room for the Q tile is reserved whenever the padded tile fits the budget, so the
-// score kernel's occupancy (and the chunking derived from it) does not depend on the
-// plan; under a multi-query plan the kernel reads each wave's current query from
-// global memory (L2-resident) instead of staging one.
-bool q_staged(const Config &c) { return q_lds_bytes(c) <= kMaxQLdsBytes; }
-
-// Dynamic LDS of the score kernel: the Q tile (if it fits), then one staging tile per
-// wave, 16 rows of (d/8 | 1) 16-byte chunks, plus one slot that lanes with nothing to
-// stage write.
 // Kernel formats: bit 0 = bf16 query (MAXSIM_BF16), bit 1 = docs stored as FP8 E4M3.
 constexpr int kFmtFp8Docs = 2;
 
+// Whether a launch stages the query tiles in LDS: whenever the padded tile fits the
+// budget. The reservation depends on the configuration alone, never on the plan, so the
+// score kernel's occupancy (and the chunking derived from it) is the same for every plan
+// and the staged maxsim_score / maxsim_finish serve both; under a multi-query plan the
+// kernel reads each wave's current query from global memory instead.
+bool q_staged(const Config &c) { return q_lds_bytes(c) <= kMaxQLdsBytes; }
+
+// Dynamic LDS of the score kernel. FP8 docs: the Q tile (if staged), then one staging
+// tile per wave, 16 rows of (d/16 | 1) 16-byte chunks, plus one slot that lanes with
+// nothing to stage write. 16-bit docs: P LDS-DMA slots per wave (dma_pipe,
+// dma_tile_bytes); a query of several register groups stays staged in front of them,
+// while a single group's fragments are loaded once per wave at the start and the slots
+// then reuse the query's LDS.
 size_t score_lds_bytes(const Config &c, int32_t d, int fmt)
 {
-    const int chunks = (fmt & kFmtFp8Docs) ? d / 16 : d / 8;
-    return (q_staged(c) ? q_lds_bytes(c) : 0) + (size_t)kScoreWaves * (kTileRows * (chunks | 1) + 1) * 16;
+    const size_t q = q_staged(c) ? q_lds_bytes(c) : 0;
+    if (fmt & kFmtFp8Docs) return q + (size_t)kScoreWaves * (kTileRows * ((d / 16) | 1) + 1) * 16;
+    const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt) * dma_tile_bytes(c.nks);
+    if (c.ngroups > 1) return q + slots;
+    return q > slots ? q : slots;
 }
 
 const void *score_fn(int fmt, const Config &c)

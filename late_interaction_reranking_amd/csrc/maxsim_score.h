@@ -81,9 +81,11 @@ constexpr int kBufferWord3 = 0x00020000;
 // exactly once; with the default policy the same stream runs ~12 % slower on MI355X
 // (6.2 vs 6.9 TB/s measured for plain 1 KB-per-instruction reads).
 constexpr int kDocLoadPolicy = 2;
-// s_waitcnt operand (gfx9 encoding) that waits for every vector memory load of the
-// wave: vmcnt 0, expcnt and lgkmcnt at their maxima (no wait on them).
-constexpr int kWaitAllVmem = 0x0F70;
+// s_waitcnt operands (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt 6:4, lgkmcnt
+// 11:8; a counter at its maximum is not waited for).
+constexpr int wait_vmcnt(int n) { return 0x0F70 | (n & 15) | ((n >> 4) << 14); }
+constexpr int kWaitAllVmem = wait_vmcnt(0);
+constexpr int kWaitAllLgkm = 0xC07F;  // lgkmcnt 0
 
 template <bool BF16>
 __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c)
@@ -154,8 +156,13 @@ __global__ void __launch_bounds__(kScoreBlock, MINW)
 score_kernel(const ScoreArgs a)
 {
     constexpr int DPAD = NKS * kStepK;
-    // 1 KB loads per 16-row doc tile: 16 rows of d elements of 2 (or 1) bytes.
-    constexpr int NLD = FP8D ? (NKS + 1) / 2 : NKS;
+    // 16-bit docs are loaded with LDS-DMA straight into the wave's P tile slots; FP8 docs
+    // with register loads (1 KB each, 16 rows of d bytes per tile) staged through LDS.
+    constexpr bool DMA = !FP8D;
+    constexpr int CP = dma_row_chunks(NKS);       // slot row: 16-byte chunks (16-bit docs)
+    constexpr int NLDD = CP / 4;                  // LDS-DMA loads per tile, 64 chunks each
+    constexpr int TILE_CHUNKS = kTileRows * CP;
+    constexpr int NLD = (NKS + 1) / 2;            // register loads per FP8 tile
     constexpr int LDQ = DPAD + 8;  // LDS row pitch (halves): 16 B skew against bank conflicts
     constexpr float NEG_INF = -__builtin_huge_valf();
 
@@ -198,9 +205,36 @@ score_kernel(const ScoreArgs a)
     const int row_in_tile = lane & 15;
     const int kgroup = lane >> 4;
     const int C = FP8D ? a.d / 16 : a.d / 8;  // 16-byte chunks per doc row
+    // The staged query stays in LDS for the whole launch for FP8 docs and for a query of
+    // several register groups; otherwise (one group, 16-bit docs) the waves load their
+    // fragments right away and the doc-tile slots reuse its LDS.
+    const bool q_keep = a.q_in_lds && (FP8D || ngroups > 1);
+    u32x4 *const tiles = reinterpret_cast<u32x4 *>(qs + (q_keep ? lq_pad * LDQ : 0));
+
+    // 16-bit docs: slot row r keeps its chunk c at position r * CP + (c ^ (r % CP)), so
+    // the 16 rows that one fragment read touches fall in distinct banks; load s, lane l
+    // fills position 64 s + l (LDS-DMA writes lane-ordered). Chunks past the row (c >= C)
+    // and rows past the tile's valid rows are outside the descriptor's range and land as
+    // zeros, so K-columns past d need no masking.
+    u32x4 *const slots = tiles + wave * (P * TILE_CHUNKS);
+    uint32_t dma_off[NLDD];
+#pragma unroll
+    for (int s = 0; s < NLDD; ++s) {
+        const int q = s * kWave + lane;
+        const int row = q / CP;
+        const int c = (q % CP) ^ (row % CP);
+        dma_off[s] = c < C ? (uint32_t)row * stride_bytes + (uint32_t)c * 16u : (uint32_t)kTileRows * stride_bytes;
+    }
+    // B fragment of K-step s: row row_in_tile, chunk kgroup + 4 s.
+    int rd_dma[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) rd_dma[s] = row_in_tile * CP + ((kgroup + 4 * s) ^ (row_in_tile % CP));
+
+    // FP8 docs: one staging buffer per wave, rows C | 1 chunks apart (odd pitch: no bank
+    // conflicts on the fragment reads).
     const int pitch = C | 1;         // LDS row pitch in chunks
     const int dummy = kTileRows * pitch;  // LDS slot for lanes with nothing to stage
-    u32x4 *tile = reinterpret_cast<u32x4 *>(qs + (a.q_in_lds ? lq_pad * LDQ : 0)) + wave * (dummy + 1);
+    u32x4 *tile = tiles + wave * (dummy + 1);
     uint32_t ld_off[NLD];            // byte offset in the tile of load s
     int st_idx[NLD];                 // LDS chunk index it is staged to
 #pragma unroll
@@ -213,9 +247,8 @@ score_kernel(const ScoreArgs a)
         ld_off[s] = ok ? (uint32_t)row * stride_bytes + (uint32_t)ch * 16u : (uint32_t)kTileRows * stride_bytes;
         st_idx[s] = ok ? row * pitch + ch : dummy;
     }
-    // B fragment of K-step s: row row_in_tile, columns 32 s + 8 kgroup .. + 7, i.e. chunk
-    // rd_idx + 4 s (16-bit docs), or 8 bytes at rd8 + 32 s (FP8 docs).
-    const int rd_idx = row_in_tile * pitch + kgroup;
+    // B fragment of K-step s: row row_in_tile, columns 32 s + 8 kgroup .. + 7, i.e. the
+    // 8 bytes at rd8 + 32 s.
     const int rd8 = (row_in_tile * pitch + (kgroup >> 1)) * 16 + (kgroup & 1) * 8;
     // K-step NKS-1 may hold 8-column groups past d: those fragment lanes are zero.
     const bool last_chunk_ok = (NKS - 1) * 4 + kgroup < a.d / 8;
@@ -309,7 +342,7 @@ score_kernel(const ScoreArgs a)
         return sp;
     };
 
-    u32x4 buf[P][NLD];
+    u32x4 buf[DMA ? 1 : P][NLD];
     // Loads of tile t of span sp into pipeline slot `slot`. The descriptor covers only
     // the tile's valid rows (none for t past the span, or for an invalid span).
     auto issue = [&](int slot, uint64_t base, int nrows, int t) {
@@ -318,31 +351,46 @@ score_kernel(const ScoreArgs a)
         const uint64_t ub = wave_uniform64(base + (uint64_t)t * kTileRows * stride_bytes);
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             reinterpret_cast<void *>((uintptr_t)ub), (short)0, (int)wave_uniform(rows * stride_bytes), kBufferWord3);
+        if constexpr (DMA) {
+            // The slot's previous tile has been read (its products were issued after the
+            // reads completed); the wait makes that explicit before it is overwritten.
+            __builtin_amdgcn_s_waitcnt(kWaitAllLgkm);
 #pragma unroll
-        for (int s = 0; s < NLD; ++s)
-            buf[slot][s] = __builtin_bit_cast(
-                u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)ld_off[s], 0, kDocLoadPolicy));
+            for (int s = 0; s < NLDD; ++s)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rsrc, (__attribute__((address_space(3))) void *)(slots + slot * TILE_CHUNKS + s * kWave), 16,
+                    (int)dma_off[s], 0, 0, kDocLoadPolicy);
+        } else {
+#pragma unroll
+            for (int s = 0; s < NLD; ++s)
+                buf[slot][s] = __builtin_bit_cast(
+                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)ld_off[s], 0, kDocLoadPolicy));
+        }
     };
 
     float rmax[NQT][4];
     // Tile t (in slot `slot`) of a span with `nrows` rows: stage, multiply, max.
     auto consume = [&](int slot, int nrows, int t) {
         const int left = nrows - t * kTileRows;
-        // Coalesced layout -> MFMA B-fragment layout through this wave's LDS buffer
-        // (the LDS operations of one wave complete in order).
-#pragma unroll
-        for (int s = 0; s < NLD; ++s) tile[st_idx[s]] = buf[slot][s];
         u32x4 bf[NKS];
+        if constexpr (DMA) {
+            // Every slot is refilled in turn, so exactly NLDD (P - 1) loads were issued
+            // after this slot's; once no more are in flight, its tile is in LDS.
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt(NLDD * (P - 1)));
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            if constexpr (FP8D) {
+            for (int s = 0; s < NKS; ++s) bf[s] = slots[slot * TILE_CHUNKS + rd_dma[s]];
+        } else {
+            // Coalesced layout -> MFMA B-fragment layout through this wave's LDS buffer
+            // (the LDS operations of one wave complete in order).
+#pragma unroll
+            for (int s = 0; s < NLD; ++s) tile[st_idx[s]] = buf[slot][s];
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
                 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
                 const u32x2 v = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const char *>(tile) + rd8 + 32 * s);
                 bf[s] = e4m3x8_to_16<BF16>(v[0], v[1]);
-            } else {
-                bf[s] = tile[rd_idx + 4 * s];
+                if (s == NKS - 1 && !last_chunk_ok) bf[s] = u32x4{0u, 0u, 0u, 0u};
             }
-            if (s == NKS - 1 && !last_chunk_ok) bf[s] = u32x4{0u, 0u, 0u, 0u};
         }
         // The accumulator starts at 0 for this lane's doc row if the row is valid and
         // at -inf if not (past the doc end): -inf + a finite dot stays -inf, so invalid
@@ -369,6 +417,14 @@ score_kernel(const ScoreArgs a)
     Span cur = resolve(g0, i0, d0);
     Span nxt = resolve(g1, i1, d1);
     uint32_t g2 = g1;
+
+    if (stage_q && !q_keep) {
+        // One register group over a staged query: load it now, before the tile slots
+        // overwrite its LDS (every wave has its fragments once the barrier is passed).
+        load_q(0, 0, 0);
+        loaded_query = 0;
+        __syncthreads();
+    }
 
 #pragma unroll
     for (int p = 0; p < P; ++p) {

@@ -19,9 +19,10 @@ namespace {
 constexpr int NKS = MAXSIM_NKS;
 constexpr bool BF = MAXSIM_BF16 != 0;
 constexpr bool FP8 = MAXSIM_FP8 != 0;
-constexpr int NLD = FP8 ? (NKS + 1) / 2 : NKS;  // 1 KB loads per doc tile
-// Register estimate of one wave: query fragments, P tiles of loads in flight, one
-// staged fragment set, running maxima and accumulators, plus addressing and loop state.
+constexpr int NLD = (NKS + 1) / 2;  // 1 KB register loads per FP8 doc tile
+// FP8 docs are loaded into registers and staged through LDS. Register estimate of one
+// wave: query fragments, P tiles of loads in flight, one staged fragment set, running
+// maxima and accumulators, plus addressing and loop state.
 template <int NQT>
 constexpr int reg_estimate(int p)
 {
@@ -31,35 +32,28 @@ constexpr int reg_estimate(int p)
 // Waves per SIMD that a register need allows (512 / waves registers each).
 constexpr int waves_for(int regs) { return regs <= 128 ? 4 : (regs <= 168 ? 3 : (regs <= 256 ? 2 : 1)); }
 
-// Pipeline depth in doc tiles: at least 4-8 KB of coalesced loads in flight per wave
-// (FP8 tiles are half the bytes, so twice as many), then deeper while the instance
-// keeps the occupancy it has at that depth (up to 4 tiles of 16-bit docs).
+// Pipeline depth in doc tiles. 16-bit docs: the LDS-DMA rule shared with the host
+// (maxsim::dma_pipe). FP8 docs: 8-16 KB of coalesced loads in flight per wave.
 template <int NQT>
 constexpr int pipe_depth()
 {
-#ifdef MAXSIM_FORCE_P
-    return MAXSIM_FORCE_P;
-#else
-    constexpr int base16 = NKS >= 3 ? 2 : (NKS == 2 ? 3 : 4);
     if constexpr (FP8) {
+        constexpr int base16 = NKS >= 3 ? 2 : (NKS == 2 ? 3 : 4);
         return 2 * base16 < 8 ? 2 * base16 : 8;
     } else {
-        int p = base16;
-        while (p < 4 && waves_for(reg_estimate<NQT>(p + 1)) == waves_for(reg_estimate<NQT>(base16))) ++p;
-        return p;
+        return maxsim::dma_pipe(NKS, NQT);
     }
-#endif
 }
 
-// Occupancy target (waves per SIMD) for the register allocation.
+// Occupancy target (workgroups of 4 waves per CU, i.e. waves per SIMD) for the register
+// allocation.
 template <int NQT>
 constexpr int min_waves()
 {
-#ifdef MAXSIM_FORCE_MINW
-    return MAXSIM_FORCE_MINW;
-#else
-    return waves_for(reg_estimate<NQT>(pipe_depth<NQT>()));
-#endif
+    if constexpr (FP8)
+        return waves_for(reg_estimate<NQT>(pipe_depth<NQT>()));
+    else
+        return maxsim::dma_blocks(NKS, NQT);
 }
 
 template <int NQT>
