@@ -231,6 +231,12 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--topk", type=int, default=0,
                     help="also select the k best docs on the GPU in every step (maxsim_topk)")
+    ap.add_argument("--short", action="store_true",
+                    help="single-query workloads: one launch per step, one workgroup per doc "
+                         "(maxsim_rerank_short) instead of plan + score + combine")
+    ap.add_argument("--graph", action="store_true",
+                    help="time the steps as replays of one step captured in a HIP graph (no host "
+                         "launch cost per kernel); the per-launch roofline still comes from eager steps")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one plain 2 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -281,6 +287,9 @@ def main() -> int:
     else:
         def plan():
             lir.maxsim_plan(offs, lens, w.Lq, w.d, ws)
+    if args.short and (w.shared_docs or w.multi_query or w.X8 is not None or args.topk):
+        print("--short applies to single-query 16-bit workloads without --topk", file=sys.stderr)
+        return 2
     if args.topk:
         if w.shared_docs or w.multi_query:
             print("--topk applies to single-query workloads", file=sys.stderr)
@@ -302,6 +311,13 @@ def main() -> int:
                 lir.maxsim_rerank_multi_fp8(Q, q_lengths, X, offs, lens, w.doc_scale, scores=scores)
             else:
                 lir.rerank_multi(Q, q_lengths, X, offs, lens, scores=scores)
+            if ev_b is not None:
+                ev_b.record()
+            return
+        if args.short:
+            if ev_a is not None:
+                ev_a.record()
+            lir.maxsim_rerank_short(Q, X, offs, lens, scores=scores)
             if ev_b is not None:
                 ev_b.record()
             return
@@ -349,6 +365,29 @@ def main() -> int:
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, score kernel {score_avg_ms:.4f} ms avg "
         f"(min {min(score_ms):.4f}, max {max(score_ms):.4f})")
 
+    ms_per_step_eager = ms_per_step
+    if args.graph:
+        # One whole step (every launch of it) captured once and replayed: the inputs stay
+        # where they are, and every replay redoes all of the step's work.
+        cap = torch.cuda.Stream()
+        cap.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(cap):
+            step()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=cap):
+            step()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+        start.record()
+        for _ in range(args.steps):
+            graph.replay()
+        end.record()
+        torch.cuda.synchronize()
+        ms_per_step = start.elapsed_time(end) / args.steps
+        log(f"timed {args.steps} graph replays: {ms_per_step:.4f} ms/step (eager {ms_per_step_eager:.4f})")
+
     if args.copy_probe:
         n = 1 << 30
         src = torch.empty(n, dtype=torch.float16, device=dev)
@@ -392,6 +431,11 @@ def main() -> int:
             "queries": w.nq,
             "parallelism": "1 GPU",
         },
+        "launch": ("HIP graph replay of one captured step" if args.graph
+                   else "eager: one host launch per kernel"),
+        "path": ("one launch, one workgroup per doc (maxsim_rerank_short)" if args.short
+                 else "scheduled: plan, score, combine"),
+        "ms_per_step_eager": ms_per_step_eager,
         "value_counts": ("each (query, doc token) pair once" if w.shared_docs else "each doc token once"),
         "hbm_GBps_step": alg_bytes / (ms_per_step * 1e-3) / 1e9,
         "pct_of_hbm_peak_step": 100.0 * alg_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
@@ -399,12 +443,13 @@ def main() -> int:
         "roofline": {
             "bound": "hbm",
             "kernel": ("score_kernel (per pass: the maxsim_rerank_multi call's time, plan and combines "
-                       "included, over its score launches)" if w.shared_docs else "score_kernel"),
+                       "included, over its score launches)" if w.shared_docs
+                       else ("short_kernel" if args.short else "score_kernel")),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": measured_traffic(w.name),
+            "traffic": None if args.short else measured_traffic(w.name),
             "algorithmic_bytes_per_launch": launch_bytes,
             "avg_launch_ms": launch_ms,
             "launches_per_step": launches,

@@ -89,6 +89,28 @@ MAXSIM_API int maxsim_rerank_bf16(const void *Q, int32_t Lq, int32_t d,
                        float *scores, void *stream);
 
 /*
+ * The same scores in a single launch, with no schedule and no scratch space: one
+ * workgroup per doc, its four waves taking the doc's 16-row tiles in turn (one program
+ * per doc, as in the Flash-MaxSim rerank page's kernel, section
+ * `_maxsim_rerank_kernel`, with the doc's tiles shared by four waves). For small
+ * batches of short docs, such as a ColBERT-style rerank of about a thousand docs of a
+ * few hundred rows, the scheduled maxsim_rerank spends most of its time in its three
+ * dependent launches. A launch here lasts as long as its longest doc, so long or very
+ * unequal docs belong on maxsim_rerank.
+ * dtype: MAXSIM_F16 or MAXSIM_BF16 (Q and docs). Scores are bitwise those of
+ * maxsim_rerank: the max is exact and the sum runs in the same order. Allocates
+ * nothing; can be captured in a graph.
+ * Errors: as maxsim_rerank, plus MAXSIM_ERR_UNSUPPORTED when the query needs more than
+ * one register group of query tiles (more than 32 16x32 query fragments: Lq > 128 at
+ * d <= 128, Lq > 64 at d <= 256, in general ceil(Lq/16) * ceil(d/32) > 32 or
+ * ceil(Lq/16) > 8).
+ */
+MAXSIM_API int maxsim_rerank_short(int dtype, const void *Q, int32_t Lq, int32_t d,
+                        const void *docs, int64_t stride,
+                        const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                        float *scores, void *stream);
+
+/*
  * Many queries in one launch ("pairs": each doc is scored against its own query).
  * The Flash-MaxSim rerank page (docs.vllm.ai, vllm.v1.pool.flash_maxsim.
  * flash_maxsim_rerank, kernel section `_maxsim_rerank_kernel`) refers to a pairs

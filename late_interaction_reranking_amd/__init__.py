@@ -30,6 +30,7 @@ from .maxsim import (  # noqa: F401
     maxsim_rerank_pairs,
     maxsim_rerank_pairs_bf16,
     maxsim_rerank_pairs_fp8,
+    maxsim_rerank_short,
     maxsim_rerank_topk,
     maxsim_topk,
     maxsim_finish,
@@ -43,4 +44,5 @@ from .maxsim import (  # noqa: F401
     rerank,
     rerank_multi,
     rerank_pairs,
+    rerank_short,
 )

@@ -171,6 +171,17 @@ constexpr int dma_pipe(int nks, int nqt)
     return p;
 }
 
+// ---------------------------------------------------------------- one-launch short-doc kernel
+struct ShortArgs {
+    const uint16_t *Q;        // [Lq, d]
+    const char *docs;         // row r at docs + r * stride_bytes
+    int64_t stride_bytes;
+    const int32_t *offsets;   // [B]
+    const int32_t *lengths;   // [B]
+    float *scores;            // [B]
+    int32_t B, d, Lq;
+};
+
 // ---------------------------------------------------------------- combine kernel
 struct CombineArgs {
     const Header *hdr;

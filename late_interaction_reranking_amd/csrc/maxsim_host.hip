@@ -44,6 +44,34 @@ MAXSIM_DECLARE_LOOKUPS(f16_fp8)
 MAXSIM_DECLARE_LOOKUPS(bf16_fp8)
 #undef MAXSIM_DECLARE_LOOKUPS
 
+// One-launch short-doc kernels, one lookup per (format, K-steps) file of 16-bit docs.
+#define MAXSIM_DECLARE_SHORT(fmt)                                                   \
+    const void *maxsim_short_kernel_##fmt##_k1(int);                               \
+    const void *maxsim_short_kernel_##fmt##_k2(int);                               \
+    const void *maxsim_short_kernel_##fmt##_k3(int);                               \
+    const void *maxsim_short_kernel_##fmt##_k4(int);                               \
+    const void *maxsim_short_kernel_##fmt##_k5(int);                               \
+    const void *maxsim_short_kernel_##fmt##_k6(int);                               \
+    const void *maxsim_short_kernel_##fmt##_k7(int);                               \
+    const void *maxsim_short_kernel_##fmt##_k8(int);                               \
+    const void *maxsim_short_kernel_##fmt(int nks, int nqt)                        \
+    {                                                                              \
+        switch (nks) {                                                             \
+        case 1: return maxsim_short_kernel_##fmt##_k1(nqt);                        \
+        case 2: return maxsim_short_kernel_##fmt##_k2(nqt);                        \
+        case 3: return maxsim_short_kernel_##fmt##_k3(nqt);                        \
+        case 4: return maxsim_short_kernel_##fmt##_k4(nqt);                        \
+        case 5: return maxsim_short_kernel_##fmt##_k5(nqt);                        \
+        case 6: return maxsim_short_kernel_##fmt##_k6(nqt);                        \
+        case 7: return maxsim_short_kernel_##fmt##_k7(nqt);                        \
+        case 8: return maxsim_short_kernel_##fmt##_k8(nqt);                        \
+        default: return nullptr;                                                   \
+        }                                                                          \
+    }
+MAXSIM_DECLARE_SHORT(f16)
+MAXSIM_DECLARE_SHORT(bf16)
+#undef MAXSIM_DECLARE_SHORT
+
 namespace {
 
 // ---------------------------------------------------------------- plan kernels
@@ -701,6 +729,48 @@ int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, in
     return run_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, stream);
 }
 
+// One launch, one workgroup per doc (csrc/maxsim_short.h); the query must fit one
+// register group.
+int rerank_short(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                 const int32_t *offsets, const int32_t *lengths, int32_t B, float *scores, void *stream_ptr)
+{
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
+    const int st = check_common(Q, Lq, d, docs, stride, offsets, lengths, B, scores);
+    if (st != MAXSIM_OK) return st;
+    const Config c = choose_config(Lq, d);
+    if (Lq > 0 && c.ngroups != 1) return MAXSIM_ERR_UNSUPPORTED;
+    if (B == 0) return MAXSIM_OK;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    if (Lq == 0) return launch_fill(scores, B, 0.0f, stream);
+    const void *fn = dtype == MAXSIM_BF16 ? maxsim_short_kernel_bf16(c.nks, c.nqt) : maxsim_short_kernel_f16(c.nks, c.nqt);
+    if (!fn) return MAXSIM_ERR_UNSUPPORTED;
+    // The query tile first, then the tile slots over it (the same LDS-DMA rule as the
+    // scheduled kernel).
+    const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt) * dma_tile_bytes(c.nks);
+    const size_t lds = q_lds_bytes(c) > slots ? q_lds_bytes(c) : slots;
+    int per_cu = 0;
+    if (score_blocks_per_cu(fn, lds, &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    DeviceFacts f;
+    if (current_facts(&f) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    // One workgroup per doc, up to four rounds of resident workgroups (each stages the
+    // query once, then takes docs b, b + grid, ...).
+    const int64_t cap = (int64_t)f.cus * per_cu * 4;
+    const unsigned grid = (unsigned)((int64_t)B < cap ? (int64_t)B : cap);
+    ShortArgs a;
+    a.Q = static_cast<const uint16_t *>(Q);
+    a.docs = static_cast<const char *>(docs);
+    a.stride_bytes = stride * 2;
+    a.offsets = offsets;
+    a.lengths = lengths;
+    a.scores = scores;
+    a.B = B;
+    a.d = d;
+    a.Lq = Lq;
+    void *args[] = {&a};
+    if (hipLaunchKernel(fn, dim3(grid), dim3(kScoreBlock), args, lds, stream) != hipSuccess) return MAXSIM_ERR_HIP;
+    return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
+}
+
 // Scores into a stream-ordered temporary buffer, then the device top-k of them.
 int rerank_topk(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
                 const int32_t *offsets, const int32_t *lengths, int32_t B, int32_t k, float *top_scores,
@@ -940,6 +1010,13 @@ int maxsim_rerank_bf16(const void *Q, int32_t Lq, int32_t d, const void *docs, i
                        float *scores, void *stream)
 {
     return rerank(MAXSIM_BF16, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores, stream);
+}
+
+int maxsim_rerank_short(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                        const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, float *scores,
+                        void *stream)
+{
+    return rerank_short(dtype, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores, stream);
 }
 
 int maxsim_rerank_pairs(const void *Qs, int32_t q_rows, int32_t d, const int32_t *q_offsets,

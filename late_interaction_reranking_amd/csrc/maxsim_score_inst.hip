@@ -1,8 +1,9 @@
 // Score kernel instances for one query format, one doc storage and one K-step count,
 // chosen by -DMAXSIM_BF16=0|1 -DMAXSIM_FP8=0|1 -DMAXSIM_NKS=1..8 (the build compiles
 // this file once per triple, in parallel). Query tiles per group NQT run 1..8 with
-// NQT * NKS <= 32.
+// NQT * NKS <= 32. Files for 16-bit docs also hold the one-launch short-doc kernel.
 #include "maxsim_score.h"
+#include "maxsim_short.h"
 
 #ifndef MAXSIM_BF16
 #error "define MAXSIM_BF16"
@@ -57,6 +58,15 @@ constexpr int min_waves()
 }
 
 template <int NQT>
+const void *short_entry()
+{
+    if constexpr (!FP8 && NQT * NKS <= maxsim::kMaxFragsPerGroup)
+        return reinterpret_cast<const void *>(&maxsim::short_kernel<NKS, NQT, BF, pipe_depth<NQT>(), min_waves<NQT>()>);
+    else
+        return nullptr;
+}
+
+template <int NQT>
 const void *entry()
 {
     if constexpr (NQT * NKS <= maxsim::kMaxFragsPerGroup)
@@ -94,3 +104,26 @@ const void *MAXSIM_LOOKUP(int nqt)
     default: return nullptr;
     }
 }
+
+#if !MAXSIM_FP8
+#if MAXSIM_BF16
+#define MAXSIM_SHORT_LOOKUP MAXSIM_CAT(maxsim_short_kernel_bf16_k, MAXSIM_NKS)
+#else
+#define MAXSIM_SHORT_LOOKUP MAXSIM_CAT(maxsim_short_kernel_f16_k, MAXSIM_NKS)
+#endif
+
+const void *MAXSIM_SHORT_LOOKUP(int nqt)
+{
+    switch (nqt) {
+    case 1: return short_entry<1>();
+    case 2: return short_entry<2>();
+    case 3: return short_entry<3>();
+    case 4: return short_entry<4>();
+    case 5: return short_entry<5>();
+    case 6: return short_entry<6>();
+    case 7: return short_entry<7>();
+    case 8: return short_entry<8>();
+    default: return nullptr;
+    }
+}
+#endif

@@ -62,6 +62,8 @@ __all__ = [
     "maxsim_finish",
     "maxsim_version",
     "rerank",
+    "maxsim_rerank_short",
+    "rerank_short",
     "maxsim_rerank_pairs",
     "maxsim_rerank_pairs_bf16",
     "maxsim_plan_pairs",
@@ -117,6 +119,8 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = rr
+        lib.maxsim_rerank_short.restype = ctypes.c_int
+        lib.maxsim_rerank_short.argtypes = [ctypes.c_int, *rr]
         lib.maxsim_status_string.restype = ctypes.c_char_p
         lib.maxsim_status_string.argtypes = [ctypes.c_int]
         lib.maxsim_workspace_size.restype = ctypes.c_int
@@ -238,6 +242,28 @@ def rerank(Q, docs, doc_offsets, doc_lengths, scores=None) -> torch.Tensor:
     if Q.dtype == torch.bfloat16:
         return maxsim_rerank_bf16(Q, docs, doc_offsets, doc_lengths, scores)
     return maxsim_rerank(Q, docs, doc_offsets, doc_lengths, scores)
+
+
+def maxsim_rerank_short(Q, docs, doc_offsets, doc_lengths, scores=None) -> torch.Tensor:
+    """fp32 [B] MaxSim scores in one launch, one workgroup per doc (for batches of short
+    docs); fp16 or bf16 by Q's dtype. Bitwise equal to maxsim_rerank."""
+    dtype = torch.bfloat16 if Q.dtype == torch.bfloat16 else torch.float16
+    Lq, d, stride, B = _marshal(Q, docs, doc_offsets, doc_lengths, dtype)
+    if scores is None:
+        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
+    elif scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    code = MAXSIM_BF16 if dtype == torch.bfloat16 else MAXSIM_F16
+    with torch.cuda.device(docs.device):
+        st = load().maxsim_rerank_short(
+            code, Q.data_ptr(), Lq, d, docs.data_ptr(), stride, doc_offsets.data_ptr(),
+            doc_lengths.data_ptr(), B, scores.data_ptr(), _stream(docs),
+        )
+    _check(st, "maxsim_rerank_short")
+    return scores
+
+
+rerank_short = maxsim_rerank_short
 
 
 def maxsim_workspace_size(Lq: int, d: int, B: int, device=None) -> int:

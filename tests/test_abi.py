@@ -36,7 +36,7 @@ def test_header_declares_the_boundary():
               "maxsim_plan_pairs", "maxsim_rerank_multi", "maxsim_rerank_multi_bf16",
               "maxsim_rerank_fp8", "maxsim_rerank_fp8_bf16", "maxsim_score_fp8", "maxsim_finish_fp8",
               "maxsim_topk_workspace_size", "maxsim_topk", "maxsim_rerank_topk", "maxsim_rerank_topk_bf16",
-              "maxsim_rerank_pairs_fp8", "maxsim_rerank_multi_fp8"):
+              "maxsim_rerank_pairs_fp8", "maxsim_rerank_multi_fp8", "maxsim_rerank_short"):
         assert n in names
 
 
@@ -94,6 +94,35 @@ def call(lib, fn="maxsim_rerank", Q=FAKE, Lq=32, d=128, docs=FAKE, stride=128, o
 ])
 def test_host_validation(lib, fn, kw, code):
     assert call(lib, fn, **kw) == code
+
+
+def call_short(lib, dtype=0, **kw):
+    args = dict(Q=FAKE, Lq=32, d=128, docs=FAKE, stride=128, offs=FAKE, lens=FAKE + 1024, B=10,
+                scores=FAKE + 4096)
+    args.update(kw)
+    return lib.maxsim_rerank_short(dtype, args["Q"], args["Lq"], args["d"], args["docs"], args["stride"],
+                                   args["offs"], args["lens"], args["B"], args["scores"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), INVALID),
+    (dict(dtype=-1), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(stride=64), INVALID),
+    (dict(scores=None), INVALID),
+    (dict(d=12, stride=16), UNSUPPORTED),
+    (dict(Lq=257), UNSUPPORTED),
+    (dict(Q=FAKE + 4), UNSUPPORTED),
+    # more than one register group of query tiles
+    (dict(Lq=129, d=128), UNSUPPORTED),
+    (dict(Lq=65, d=256, stride=256), UNSUPPORTED),
+    (dict(Lq=97, d=160, stride=160), UNSUPPORTED),   # 7 query tiles of 5 K-steps: 35 > 32
+    (dict(Lq=129, d=128, B=0), UNSUPPORTED),         # the envelope is checked before B
+    (dict(B=0, docs=None, offs=None, lens=None, scores=None), OK),
+    (dict(dtype=1, B=0, docs=None, offs=None, lens=None, scores=None), OK),
+])
+def test_short_validation(lib, kw, code):
+    assert call_short(lib, **kw) == code
 
 
 def test_staged_validation(lib):
