@@ -135,39 +135,50 @@ struct ScoreArgs {
 constexpr size_t kMaxQLdsBytes = 64 * 1024;
 
 // ---------------------------------------------------------------- doc-tile pipeline
-// 16-bit docs go from memory straight into LDS (LDS-DMA buffer loads, 16 bytes per
-// lane, no registers in flight). A 16-row tile is kept as rows of dma_row_chunks(NKS)
-// 16-byte chunks: a power of two >= the d / 8 chunks of a row, the rest filled with
-// zeros by out-of-range loads. Each wave owns P such slots. These rules fix an
-// instance's pipeline depth and the occupancy it is built for; the host sizes the
-// kernel's LDS with the same functions.
+// Doc tiles go from memory straight into LDS (LDS-DMA buffer loads, 16 bytes per lane,
+// no registers in flight). A 16-row tile is kept as rows of dma_row_chunks 16-byte
+// chunks: a power of two covering the K-steps' columns (8 elements per chunk for 16-bit
+// docs, 16 for FP8 docs), the chunks past a row's d columns filled with zeros by
+// out-of-range loads. Each wave owns P such slots. These rules fix an instance's
+// pipeline depth and the occupancy it is built for; the host sizes the kernel's LDS
+// with the same functions.
 constexpr int kLdsPerCu = 160 * 1024;
 constexpr int kScoreStaticLds = 1024;             // bin tables and other static LDS, rounded up
 
-constexpr int dma_row_chunks(int nks) { return nks <= 1 ? 4 : (nks <= 2 ? 8 : (nks <= 4 ? 16 : 32)); }
-constexpr int dma_tile_bytes(int nks) { return kTileRows * dma_row_chunks(nks) * 16; }
-// Registers of one wave: query fragments, one B-fragment set, running maxima,
-// accumulators, addressing and loop state.
-constexpr int dma_regs(int nks, int nqt) { return 4 * nqt * nks + 4 * nks + 4 * nqt + 56; }
-constexpr int dma_waves_per_simd(int nks, int nqt)
+constexpr int dma_row_chunks(int nks, bool fp8)
 {
-    return dma_regs(nks, nqt) <= 128 ? 4 : (dma_regs(nks, nqt) <= 168 ? 3 : (dma_regs(nks, nqt) <= 256 ? 2 : 1));
+    const int need = fp8 ? 2 * nks : 4 * nks;  // chunks the NKS K-steps read
+    return need <= 4 ? 4 : (need <= 8 ? 8 : (need <= 16 ? 16 : 32));
+}
+constexpr int dma_tile_bytes(int nks, bool fp8) { return kTileRows * dma_row_chunks(nks, fp8) * 16; }
+// Swizzle of slot row r: its chunk c sits at r * CP + (c ^ dma_swizzle(r, CP)). The 16
+// rows of one fragment read land in distinct 16-byte bank groups, modulo 8 and modulo
+// 16 groups, whichever the LDS serves a read in.
+__host__ __device__ constexpr int dma_swizzle(int r, int cp) { return (r % cp) ^ ((r / cp) & 1); }
+// Registers of one wave: query fragments, one B-fragment set, running maxima,
+// accumulators, addressing and loop state (and the FP8 conversion's temporaries).
+constexpr int dma_regs(int nks, int nqt, bool fp8) { return 4 * nqt * nks + 4 * nks + 4 * nqt + 56 + (fp8 ? 8 : 0); }
+constexpr int dma_waves_per_simd(int nks, int nqt, bool fp8)
+{
+    return dma_regs(nks, nqt, fp8) <= 128 ? 4 : (dma_regs(nks, nqt, fp8) <= 168 ? 3 : (dma_regs(nks, nqt, fp8) <= 256 ? 2 : 1));
 }
 // Workgroups per CU an instance is built for: what its registers allow, at most 3 (four
 // workgroups of LDS-DMA streams per CU read slower than three, measured), and fewer if
 // two tiles in flight per wave would not fit their LDS.
-constexpr int dma_blocks(int nks, int nqt)
+constexpr int dma_blocks(int nks, int nqt, bool fp8)
 {
-    int b = dma_waves_per_simd(nks, nqt) < 3 ? dma_waves_per_simd(nks, nqt) : 3;
-    while (b > 1 && kScoreWaves * 2 * dma_tile_bytes(nks) > kLdsPerCu / b - kScoreStaticLds) --b;
+    int b = dma_waves_per_simd(nks, nqt, fp8) < 3 ? dma_waves_per_simd(nks, nqt, fp8) : 3;
+    while (b > 1 && kScoreWaves * 2 * dma_tile_bytes(nks, fp8) > kLdsPerCu / b - kScoreStaticLds) --b;
     return b;
 }
 // Tiles in flight per wave: up to 16 KB (8 tiles), within a workgroup's share of LDS.
-constexpr int dma_pipe(int nks, int nqt)
+constexpr int dma_pipe(int nks, int nqt, bool fp8)
 {
-    int p = 16384 / dma_tile_bytes(nks);
+    int p = 16384 / dma_tile_bytes(nks, fp8);
     if (p > 8) p = 8;
-    while (p > 1 && kScoreWaves * p * dma_tile_bytes(nks) > kLdsPerCu / dma_blocks(nks, nqt) - kScoreStaticLds) --p;
+    while (p > 1 &&
+           kScoreWaves * p * dma_tile_bytes(nks, fp8) > kLdsPerCu / dma_blocks(nks, nqt, fp8) - kScoreStaticLds)
+        --p;
     return p;
 }
 

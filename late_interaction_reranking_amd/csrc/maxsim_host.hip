@@ -527,17 +527,16 @@ constexpr int kFmtFp8Docs = 2;
 // kernel reads each wave's current query from global memory instead.
 bool q_staged(const Config &c) { return q_lds_bytes(c) <= kMaxQLdsBytes; }
 
-// Dynamic LDS of the score kernel. FP8 docs: the Q tile (if staged), then one staging
-// tile per wave, 16 rows of (d/16 | 1) 16-byte chunks, plus one slot that lanes with
-// nothing to stage write. 16-bit docs: P LDS-DMA slots per wave (dma_pipe,
+// Dynamic LDS of the score kernel: P LDS-DMA tile slots per wave (dma_pipe,
 // dma_tile_bytes); a query of several register groups stays staged in front of them,
 // while a single group's fragments are loaded once per wave at the start and the slots
 // then reuse the query's LDS.
 size_t score_lds_bytes(const Config &c, int32_t d, int fmt)
 {
+    (void)d;
+    const bool fp8 = (fmt & kFmtFp8Docs) != 0;
     const size_t q = q_staged(c) ? q_lds_bytes(c) : 0;
-    if (fmt & kFmtFp8Docs) return q + (size_t)kScoreWaves * (kTileRows * ((d / 16) | 1) + 1) * 16;
-    const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt) * dma_tile_bytes(c.nks);
+    const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt, fp8) * dma_tile_bytes(c.nks, fp8);
     if (c.ngroups > 1) return q + slots;
     return q > slots ? q : slots;
 }
@@ -746,7 +745,7 @@ int rerank_short(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     if (!fn) return MAXSIM_ERR_UNSUPPORTED;
     // The query tile first, then the tile slots over it (the same LDS-DMA rule as the
     // scheduled kernel).
-    const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt) * dma_tile_bytes(c.nks);
+    const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt, false) * dma_tile_bytes(c.nks, false);
     const size_t lds = q_lds_bytes(c) > slots ? q_lds_bytes(c) : slots;
     int per_cu = 0;
     if (score_blocks_per_cu(fn, lds, &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;

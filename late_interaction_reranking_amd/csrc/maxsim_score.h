@@ -20,27 +20,25 @@
 //     32-column K-steps (when the padded tile fits 64 KB; a larger query's fragments
 //     are read from global memory). Each wave keeps its MFMA A-fragments of one group
 //     of up to NQT query tiles in registers; with one group (every Lq * d that fits
-//     128 VGPRs) they are loaded once for the kernel's lifetime.
-//   - Doc rows are read in 16-row tiles with coalesced, non-temporal 128-bit buffer
-//     loads: load s, lane l takes 16-byte chunk e = 64 s + l of the tile (row e / C,
-//     chunk e % C, C = d / 8), so one load instruction reads 1 KB of consecutive row
-//     bytes. (The
-//     MFMA operand layout read straight from memory touches 16 rows x 64 B per
-//     instruction, half of 16 cache lines, and streams ~13 % slower on this chip.)
-//     Each wave then writes the tile into its own LDS buffer, rows C | 1 chunks apart
-//     (odd pitch: conflict-free reads), and reads it back in the B-fragment layout of
+//     128 VGPRs) they are loaded once, at the start, and the doc-tile slots then reuse
+//     the query's LDS.
+//   - Doc rows are read in 16-row tiles with non-temporal LDS-DMA buffer loads
+//     (buffer_load ... lds): 16 bytes per lane go straight into the wave's LDS slot,
+//     lane-ordered, so no registers hold tiles in flight and the pipeline depth is set
+//     by LDS. Each lane fetches the global chunk that belongs at its LDS position under
+//     an XOR-swizzled row layout (conflict-free fragment reads); 16 lanes still read
+//     one contiguous run of a row. Lanes then read the B-fragment layout of
 //     v_mfma_f32_16x16x32_{f16,bf16}: lane l, K-step s gets row (l % 16), columns
 //     8 (4 s + l / 16) .. +7. A and B use the same lane -> column mapping, so the dot
 //     products are exact dot products whatever the order inside a fragment.
 //   - The row address is a 64-bit scalar base (doc offset widened to int64 before it
 //     is multiplied by the stride, as the page's kernel does) plus a 32-bit per-lane
 //     offset. Each tile gets a buffer descriptor whose size covers only the tile's
-//     valid rows, so rows past the end of the doc read as zero and are never fetched;
-//     chunks past the tile (when 16 C is not a multiple of 64) are pushed out of
-//     range the same way, and K-columns past d are zeroed in the fragment.
+//     valid rows, so rows past the end of the doc are never fetched and land as zeros;
+//     chunks past the row's d columns are pushed out of range the same way.
 //   - Docs may be stored as FP8 E4M3 (half the bytes of the bandwidth-bound stream):
-//     tiles are loaded and staged as bytes, and each lane converts its 8-byte B fragment
-//     to Q's format with the hardware converter (exact), so the MFMA and the fp32
+//     tiles are loaded as bytes, and each lane converts its 8-byte B fragment to Q's
+//     format with the hardware converter (exact), so the MFMA and the fp32
 //     accumulation are the 16-bit path's; the doc tensor's scale multiplies the sum.
 //   - S = Qtile . Dtile^T lands with lane l holding doc row (l % 16) and query rows
 //     4 (l / 16) + j, j < 4. The accumulator of an invalid doc row (past the doc's
@@ -156,13 +154,10 @@ __global__ void __launch_bounds__(kScoreBlock, MINW)
 score_kernel(const ScoreArgs a)
 {
     constexpr int DPAD = NKS * kStepK;
-    // 16-bit docs are loaded with LDS-DMA straight into the wave's P tile slots; FP8 docs
-    // with register loads (1 KB each, 16 rows of d bytes per tile) staged through LDS.
-    constexpr bool DMA = !FP8D;
-    constexpr int CP = dma_row_chunks(NKS);       // slot row: 16-byte chunks (16-bit docs)
-    constexpr int NLDD = CP / 4;                  // LDS-DMA loads per tile, 64 chunks each
+    // Doc tiles are loaded with LDS-DMA straight into the wave's P tile slots.
+    constexpr int CP = dma_row_chunks(NKS, FP8D);  // slot row: 16-byte chunks
+    constexpr int NLDD = CP / 4;                   // LDS-DMA loads per tile, 64 chunks each
     constexpr int TILE_CHUNKS = kTileRows * CP;
-    constexpr int NLD = (NKS + 1) / 2;            // register loads per FP8 tile
     constexpr int LDQ = DPAD + 8;  // LDS row pitch (halves): 16 B skew against bank conflicts
     constexpr float NEG_INF = -__builtin_huge_valf();
 
@@ -208,13 +203,13 @@ score_kernel(const ScoreArgs a)
     // The staged query stays in LDS for the whole launch for FP8 docs and for a query of
     // several register groups; otherwise (one group, 16-bit docs) the waves load their
     // fragments right away and the doc-tile slots reuse its LDS.
-    const bool q_keep = a.q_in_lds && (FP8D || ngroups > 1);
+    const bool q_keep = a.q_in_lds && ngroups > 1;
     u32x4 *const tiles = reinterpret_cast<u32x4 *>(qs + (q_keep ? lq_pad * LDQ : 0));
 
-    // 16-bit docs: slot row r keeps its chunk c at position r * CP + (c ^ (r % CP)), so
-    // the 16 rows that one fragment read touches fall in distinct banks; load s, lane l
-    // fills position 64 s + l (LDS-DMA writes lane-ordered). Chunks past the row (c >= C)
-    // and rows past the tile's valid rows are outside the descriptor's range and land as
+    // Slot row r keeps its chunk c at position r * CP + (c ^ dma_swizzle(r, CP)), so the
+    // 16 rows that one fragment read touches fall in distinct banks; load s, lane l fills
+    // position 64 s + l (LDS-DMA writes lane-ordered). Chunks past the row (c >= C) and
+    // rows past the tile's valid rows are outside the descriptor's range and land as
     // zeros, so K-columns past d need no masking.
     u32x4 *const slots = tiles + wave * (P * TILE_CHUNKS);
     uint32_t dma_off[NLDD];
@@ -222,36 +217,18 @@ score_kernel(const ScoreArgs a)
     for (int s = 0; s < NLDD; ++s) {
         const int q = s * kWave + lane;
         const int row = q / CP;
-        const int c = (q % CP) ^ (row % CP);
+        const int c = (q % CP) ^ dma_swizzle(row, CP);
         dma_off[s] = c < C ? (uint32_t)row * stride_bytes + (uint32_t)c * 16u : (uint32_t)kTileRows * stride_bytes;
     }
-    // B fragment of K-step s: row row_in_tile, chunk kgroup + 4 s.
+    // B fragment of K-step s, row row_in_tile: 16-bit docs, chunk kgroup + 4 s (8
+    // columns); FP8 docs, the 8 bytes at half kgroup % 2 of chunk kgroup / 2 + 2 s.
     int rd_dma[NKS];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) rd_dma[s] = row_in_tile * CP + ((kgroup + 4 * s) ^ (row_in_tile % CP));
-
-    // FP8 docs: one staging buffer per wave, rows C | 1 chunks apart (odd pitch: no bank
-    // conflicts on the fragment reads).
-    const int pitch = C | 1;         // LDS row pitch in chunks
-    const int dummy = kTileRows * pitch;  // LDS slot for lanes with nothing to stage
-    u32x4 *tile = tiles + wave * (dummy + 1);
-    uint32_t ld_off[NLD];            // byte offset in the tile of load s
-    int st_idx[NLD];                 // LDS chunk index it is staged to
-#pragma unroll
-    for (int s = 0; s < NLD; ++s) {
-        const int e = s * kWave + lane;
-        const int row = e / C;
-        const int ch = e - row * C;
-        const bool ok = e < kTileRows * C;
-        // Chunks past the tile point at row 16, which no tile descriptor covers.
-        ld_off[s] = ok ? (uint32_t)row * stride_bytes + (uint32_t)ch * 16u : (uint32_t)kTileRows * stride_bytes;
-        st_idx[s] = ok ? row * pitch + ch : dummy;
+    for (int s = 0; s < NKS; ++s) {
+        const int c = FP8D ? (kgroup >> 1) + 2 * s : kgroup + 4 * s;
+        rd_dma[s] = row_in_tile * CP + (c ^ dma_swizzle(row_in_tile, CP));
     }
-    // B fragment of K-step s: row row_in_tile, columns 32 s + 8 kgroup .. + 7, i.e. the
-    // 8 bytes at rd8 + 32 s.
-    const int rd8 = (row_in_tile * pitch + (kgroup >> 1)) * 16 + (kgroup & 1) * 8;
-    // K-step NKS-1 may hold 8-column groups past d: those fragment lanes are zero.
-    const bool last_chunk_ok = (NKS - 1) * 4 + kgroup < a.d / 8;
+    const int rd_half = (kgroup & 1) * 8;  // FP8 docs: byte offset in the chunk
 
     // Query fragments of register group grp: from LDS when the query tiles are staged
     // there, else from global memory, by the tile table or, under a pairs plan, for the
@@ -342,7 +319,6 @@ score_kernel(const ScoreArgs a)
         return sp;
     };
 
-    u32x4 buf[DMA ? 1 : P][NLD];
     // Loads of tile t of span sp into pipeline slot `slot`. The descriptor covers only
     // the tile's valid rows (none for t past the span, or for an invalid span).
     auto issue = [&](int slot, uint64_t base, int nrows, int t) {
@@ -351,21 +327,14 @@ score_kernel(const ScoreArgs a)
         const uint64_t ub = wave_uniform64(base + (uint64_t)t * kTileRows * stride_bytes);
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             reinterpret_cast<void *>((uintptr_t)ub), (short)0, (int)wave_uniform(rows * stride_bytes), kBufferWord3);
-        if constexpr (DMA) {
-            // The slot's previous tile has been read (its products were issued after the
-            // reads completed); the wait makes that explicit before it is overwritten.
-            __builtin_amdgcn_s_waitcnt(kWaitAllLgkm);
+        // The slot's previous tile has been read (its products were issued after the
+        // reads completed); the wait makes that explicit before it is overwritten.
+        __builtin_amdgcn_s_waitcnt(kWaitAllLgkm);
 #pragma unroll
-            for (int s = 0; s < NLDD; ++s)
-                __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rsrc, (__attribute__((address_space(3))) void *)(slots + slot * TILE_CHUNKS + s * kWave), 16,
-                    (int)dma_off[s], 0, 0, kDocLoadPolicy);
-        } else {
-#pragma unroll
-            for (int s = 0; s < NLD; ++s)
-                buf[slot][s] = __builtin_bit_cast(
-                    u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc, (int)ld_off[s], 0, kDocLoadPolicy));
-        }
+        for (int s = 0; s < NLDD; ++s)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void *)(slots + slot * TILE_CHUNKS + s * kWave), 16,
+                (int)dma_off[s], 0, 0, kDocLoadPolicy);
     };
 
     float rmax[NQT][4];
@@ -373,23 +342,18 @@ score_kernel(const ScoreArgs a)
     auto consume = [&](int slot, int nrows, int t) {
         const int left = nrows - t * kTileRows;
         u32x4 bf[NKS];
-        if constexpr (DMA) {
-            // Every slot is refilled in turn, so exactly NLDD (P - 1) loads were issued
-            // after this slot's; once no more are in flight, its tile is in LDS.
-            __builtin_amdgcn_s_waitcnt(wait_vmcnt(NLDD * (P - 1)));
+        // Every slot is refilled in turn, so exactly NLDD (P - 1) loads were issued after
+        // this slot's; once no more are in flight, its tile is in LDS.
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(NLDD * (P - 1)));
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) bf[s] = slots[slot * TILE_CHUNKS + rd_dma[s]];
-        } else {
-            // Coalesced layout -> MFMA B-fragment layout through this wave's LDS buffer
-            // (the LDS operations of one wave complete in order).
-#pragma unroll
-            for (int s = 0; s < NLD; ++s) tile[st_idx[s]] = buf[slot][s];
-#pragma unroll
-            for (int s = 0; s < NKS; ++s) {
+        for (int s = 0; s < NKS; ++s) {
+            if constexpr (FP8D) {
                 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 v = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const char *>(tile) + rd8 + 32 * s);
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(
+                    reinterpret_cast<const char *>(slots + slot * TILE_CHUNKS + rd_dma[s]) + rd_half);
                 bf[s] = e4m3x8_to_16<BF16>(v[0], v[1]);
-                if (s == NKS - 1 && !last_chunk_ok) bf[s] = u32x4{0u, 0u, 0u, 0u};
+            } else {
+                bf[s] = slots[slot * TILE_CHUNKS + rd_dma[s]];
             }
         }
         // The accumulator starts at 0 for this lane's doc row if the row is valid and

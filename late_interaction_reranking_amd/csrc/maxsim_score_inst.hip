@@ -20,41 +20,19 @@ namespace {
 constexpr int NKS = MAXSIM_NKS;
 constexpr bool BF = MAXSIM_BF16 != 0;
 constexpr bool FP8 = MAXSIM_FP8 != 0;
-constexpr int NLD = (NKS + 1) / 2;  // 1 KB register loads per FP8 doc tile
-// FP8 docs are loaded into registers and staged through LDS. Register estimate of one
-// wave: query fragments, P tiles of loads in flight, one staged fragment set, running
-// maxima and accumulators, plus addressing and loop state.
-template <int NQT>
-constexpr int reg_estimate(int p)
-{
-    return 4 * NQT * NKS + 4 * p * NLD + 4 * NKS + 4 * NQT + 48;
-}
-
-// Waves per SIMD that a register need allows (512 / waves registers each).
-constexpr int waves_for(int regs) { return regs <= 128 ? 4 : (regs <= 168 ? 3 : (regs <= 256 ? 2 : 1)); }
-
-// Pipeline depth in doc tiles. 16-bit docs: the LDS-DMA rule shared with the host
-// (maxsim::dma_pipe). FP8 docs: 8-16 KB of coalesced loads in flight per wave.
+// Pipeline depth in doc tiles and occupancy target (workgroups of 4 waves per CU,
+// i.e. waves per SIMD) for the register allocation: the LDS-DMA rule shared with the
+// host (maxsim::dma_pipe, maxsim::dma_blocks).
 template <int NQT>
 constexpr int pipe_depth()
 {
-    if constexpr (FP8) {
-        constexpr int base16 = NKS >= 3 ? 2 : (NKS == 2 ? 3 : 4);
-        return 2 * base16 < 8 ? 2 * base16 : 8;
-    } else {
-        return maxsim::dma_pipe(NKS, NQT);
-    }
+    return maxsim::dma_pipe(NKS, NQT, FP8);
 }
 
-// Occupancy target (workgroups of 4 waves per CU, i.e. waves per SIMD) for the register
-// allocation.
 template <int NQT>
 constexpr int min_waves()
 {
-    if constexpr (FP8)
-        return waves_for(reg_estimate<NQT>(pipe_depth<NQT>()));
-    else
-        return maxsim::dma_blocks(NKS, NQT);
+    return maxsim::dma_blocks(NKS, NQT, FP8);
 }
 
 template <int NQT>

@@ -26,7 +26,7 @@ short_kernel(const ShortArgs a)
 {
     constexpr int DPAD = NKS * kStepK;
     constexpr int LDQ = DPAD + 8;                 // Q row pitch in LDS (halves), as the score kernel's
-    constexpr int CP = dma_row_chunks(NKS);
+    constexpr int CP = dma_row_chunks(NKS, false);
     constexpr int NLDD = CP / 4;
     constexpr int TILE_CHUNKS = kTileRows * CP;
     constexpr int LQP = NQT * kTileRows;          // padded query rows
@@ -69,12 +69,12 @@ short_kernel(const ShortArgs a)
     for (int s = 0; s < NLDD; ++s) {
         const int q = s * kWave + lane;
         const int row = q / CP;
-        const int c = (q % CP) ^ (row % CP);
+        const int c = (q % CP) ^ dma_swizzle(row, CP);
         dma_off[s] = c < C ? (uint32_t)row * stride_bytes + (uint32_t)c * 16u : (uint32_t)kTileRows * stride_bytes;
     }
     int rd_dma[NKS];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) rd_dma[s] = row_in_tile * CP + ((kgroup + 4 * s) ^ (row_in_tile % CP));
+    for (int s = 0; s < NKS; ++s) rd_dma[s] = row_in_tile * CP + ((kgroup + 4 * s) ^ dma_swizzle(row_in_tile, CP));
 
     for (uint32_t doc = blockIdx.x; doc < (uint32_t)a.B; doc += gridDim.x) {
         typedef __attribute__((address_space(4))) const int32_t ConstI32;
