@@ -360,14 +360,22 @@ score_kernel(const ScoreArgs a)
         // at -inf if not (past the doc end): -inf + a finite dot stays -inf, so invalid
         // rows never win the max and need no masking.
         const float c0 = row_in_tile < left ? 0.0f : NEG_INF;
+        // Query tile qt's products go into one accumulator while tile qt - 1's, in the
+        // other, are folded into the running max: the max waits on finished MFMAs.
+        f32x4 acc[2];
 #pragma unroll
         for (int qt = 0; qt < NQT; ++qt) {
-            f32x4 acc = {c0, c0, c0, c0};
+            f32x4 a = {c0, c0, c0, c0};
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) acc = mfma16x16x32<BF16>(qf[qt][s], bf[s], acc);
+            for (int s = 0; s < NKS; ++s) a = mfma16x16x32<BF16>(qf[qt][s], bf[s], a);
+            acc[qt & 1] = a;
+            if (qt > 0) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) rmax[qt][i] = __builtin_fmaxf(rmax[qt][i], acc[i]);
+                for (int i = 0; i < 4; ++i) rmax[qt - 1][i] = __builtin_fmaxf(rmax[qt - 1][i], acc[(qt - 1) & 1][i]);
+            }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rmax[NQT - 1][i] = __builtin_fmaxf(rmax[NQT - 1][i], acc[(NQT - 1) & 1][i]);
     };
 
     // Descriptor queue: cur and nxt resolved, the one after that in flight.

@@ -114,14 +114,23 @@ short_kernel(const ShortArgs a)
 #pragma unroll
             for (int s = 0; s < NKS; ++s) bf[s] = slots[slot * TILE_CHUNKS + rd_dma[s]];
             const float c0 = row_in_tile < left ? 0.0f : NEG_INF;
+            // Tile qt's products in one accumulator while tile qt - 1's are folded into
+            // the running max (as in the score kernel).
+            f32x4 acc[2];
 #pragma unroll
             for (int qt = 0; qt < NQT; ++qt) {
-                f32x4 acc = {c0, c0, c0, c0};
+                f32x4 r = {c0, c0, c0, c0};
 #pragma unroll
-                for (int s = 0; s < NKS; ++s) acc = mfma16x16x32<BF16>(qf[qt][s], bf[s], acc);
+                for (int s = 0; s < NKS; ++s) r = mfma16x16x32<BF16>(qf[qt][s], bf[s], r);
+                acc[qt & 1] = r;
+                if (qt > 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) rmax[qt][i] = __builtin_fmaxf(rmax[qt][i], acc[i]);
+                    for (int i = 0; i < 4; ++i)
+                        rmax[qt - 1][i] = __builtin_fmaxf(rmax[qt - 1][i], acc[(qt - 1) & 1][i]);
+                }
             }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rmax[NQT - 1][i] = __builtin_fmaxf(rmax[NQT - 1][i], acc[(NQT - 1) & 1][i]);
         };
 
         // P tiles deep; every slot is refilled in turn (zero-size loads past the wave's
