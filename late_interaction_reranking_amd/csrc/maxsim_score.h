@@ -197,6 +197,7 @@ score_kernel(const ScoreArgs a)
 
     // ---- per-lane load and staging geometry
     const uint32_t stride_bytes = (uint32_t)a.stride_bytes;
+    const uint32_t tile_bytes = (uint32_t)kTileRows * stride_bytes;  // bytes between tiles of a doc
     const int row_in_tile = lane & 15;
     const int kgroup = lane >> 4;
     const int C = FP8D ? a.d / 16 : a.d / 8;  // 16-byte chunks per doc row
@@ -322,11 +323,15 @@ score_kernel(const ScoreArgs a)
     // Loads of tile t of span sp into pipeline slot `slot`. The descriptor covers only
     // the tile's valid rows (none for t past the span, or for an invalid span).
     auto issue = [&](int slot, uint64_t base, int nrows, int t) {
-        const int left = nrows - t * kTileRows;
-        const uint32_t rows = left <= 0 ? 0u : (left >= kTileRows ? (uint32_t)kTileRows : (uint32_t)left);
-        const uint64_t ub = wave_uniform64(base + (uint64_t)t * kTileRows * stride_bytes);
+        // Valid rows of the tile, clamped in two steps on scalar registers (one clamp
+        // would become a vector med3, a vector multiply and a readfirstlane).
+        const int left = (int)wave_uniform((uint32_t)(nrows - t * kTileRows));
+        const int lo = (int)wave_uniform((uint32_t)(left > 0 ? left : 0));
+        const uint32_t rows = (uint32_t)(lo < kTileRows ? lo : kTileRows);
+        // t < 2^27 and a tile is at most 16 rows of 2^25 bytes: a 32 x 32 -> 64-bit product.
+        const uint64_t ub = wave_uniform64(base + (uint64_t)(uint32_t)t * (uint64_t)tile_bytes);
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            reinterpret_cast<void *>((uintptr_t)ub), (short)0, (int)wave_uniform(rows * stride_bytes), kBufferWord3);
+            reinterpret_cast<void *>((uintptr_t)ub), (short)0, (int)(rows * stride_bytes), kBufferWord3);
         // The slot's previous tile has been read (its products were issued after the
         // reads completed); the wait makes that explicit before it is overwritten.
         __builtin_amdgcn_s_waitcnt(kWaitAllLgkm);

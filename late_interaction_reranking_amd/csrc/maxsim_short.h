@@ -62,6 +62,7 @@ short_kernel(const ShortArgs a)
 
     // ---- LDS-DMA slots and fragment addresses (the score kernel's layout)
     const uint32_t stride_bytes = (uint32_t)a.stride_bytes;
+    const uint32_t tile_bytes = (uint32_t)kTileRows * stride_bytes;
     const int C = a.d / 8;
     u32x4 *const slots = reinterpret_cast<u32x4 *>(qs) + wave * (P * TILE_CHUNKS);
     uint32_t dma_off[NLDD];
@@ -88,11 +89,13 @@ short_kernel(const ShortArgs a)
         // Tile k of this wave (doc tile wave + 4 k) into slot `slot`; zero-size past its tiles.
         auto issue = [&](int slot, int k) {
             const int t = wave + kScoreWaves * k;
-            const int left = k < cnt ? len - t * kTileRows : 0;
-            const uint32_t rows = left <= 0 ? 0u : (left >= kTileRows ? (uint32_t)kTileRows : (uint32_t)left);
-            const uint64_t ub = wave_uniform64(base + (uint64_t)(k < cnt ? t : 0) * kTileRows * stride_bytes);
+            // Valid rows, clamped in two steps on scalar registers (as in the score kernel).
+            const int left = (int)wave_uniform((uint32_t)(k < cnt ? len - t * kTileRows : 0));
+            const int lo = (int)wave_uniform((uint32_t)(left > 0 ? left : 0));
+            const uint32_t rows = (uint32_t)(lo < kTileRows ? lo : kTileRows);
+            const uint64_t ub = wave_uniform64(base + (uint64_t)(uint32_t)(k < cnt ? t : 0) * (uint64_t)tile_bytes);
             const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
-                reinterpret_cast<void *>((uintptr_t)ub), (short)0, (int)wave_uniform(rows * stride_bytes), kBufferWord3);
+                reinterpret_cast<void *>((uintptr_t)ub), (short)0, (int)(rows * stride_bytes), kBufferWord3);
             __builtin_amdgcn_s_waitcnt(kWaitAllLgkm);
 #pragma unroll
             for (int s = 0; s < NLDD; ++s)
