@@ -8,8 +8,8 @@
 // unique and the selection is exact. Selection runs in levels: every block holds 4096
 // keys in registers, finds its k-th largest by radix selection on an LDS histogram and
 // keeps the k keys at or above it; the survivors (k per block) are the next level's
-// input, until one block remains, which sorts its k survivors (bitonic, in LDS) and
-// writes the results.
+// input, until one block remains, which places each of its k survivors at its rank
+// (the number of survivors above it, counted in LDS) and writes the results.
 // Everything stays on the stream; nothing is read back to the host.
 #include "maxsim.h"
 
@@ -38,8 +38,8 @@ __device__ __forceinline__ uint64_t rank_key(float v, uint32_t idx)
 // scores themselves when in_keys is null), finds its k-th largest key T by radix
 // selection in LDS (passes of 8 bits from the highest bit in which the block's keys
 // differ; keys are unique apart from the zero padding), and keeps the k keys >= T: unordered in out_keys[b * k ..], or, on
-// the last level (out_keys null), sorted (bitonic, descending) into the final
-// (score, index) pairs.
+// the last level (out_keys null), ranked (descending) into the final (score, index)
+// pairs.
 __global__ void __launch_bounds__(kThreads)
 topk_level_kernel(const float *__restrict__ scores, const uint64_t *__restrict__ in_keys, int64_t n,
                   int32_t k, uint64_t *__restrict__ out_keys, int32_t B, float *__restrict__ top_scores,
@@ -160,34 +160,21 @@ topk_level_kernel(const float *__restrict__ scores, const uint64_t *__restrict__
         }
     if (out_keys) return;
 
-    // Last level: sort the k survivors (padded with zeros to a power of two).
-    int np = 1;
-    while (np < k) np <<= 1;
-    __syncthreads();
-    for (int i = k + tid; i < np; i += kThreads) sel[i] = 0;
-    for (int size = 2; size <= np; size <<= 1) {
-        for (int stride = size >> 1; stride > 0; stride >>= 1) {
-            __syncthreads();
-            const int ls = __builtin_ctz(stride);
-            for (int t = tid; t < np / 2; t += kThreads) {
-                const int lo = ((t >> ls) << (ls + 1)) | (t & (stride - 1));
-                const int hi = lo + stride;
-                const bool desc = (lo & size) == 0;  // this run ends up descending
-                const uint64_t a = sel[lo], b = sel[hi];
-                if ((a < b) == desc) {
-                    sel[lo] = b;
-                    sel[hi] = a;
-                }
-            }
-        }
-    }
+    // Last level: each survivor's place in the output is its rank, the number of
+    // survivors above it (keys are unique apart from the zero padding, whose equal keys
+    // are ranked by position). One pass of k LDS reads per thread, one barrier.
     __syncthreads();
     for (int j = tid; j < k; j += kThreads) {
         const uint64_t v = sel[j];
+        int rank = 0;
+        for (int i = 0; i < k; ++i) {
+            const uint64_t u = sel[i];
+            rank += (u > v || (u == v && i < j)) ? 1 : 0;
+        }
         const uint32_t idx = 0xFFFFFFFFu - (uint32_t)v;
         const bool real = v != 0u && idx < (uint32_t)B;
-        top_ids[j] = real ? (int32_t)idx : -1;
-        top_scores[j] = real ? scores[idx] : -__builtin_huge_valf();
+        top_ids[rank] = real ? (int32_t)idx : -1;
+        top_scores[rank] = real ? scores[idx] : -__builtin_huge_valf();
     }
 }
 
