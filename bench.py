@@ -41,7 +41,7 @@ MFMA_F16_PEAK_TFLOPS = 2500.0   # dense fp16 / bf16
 METRIC = "doc tokens scored/sec and achieved HBM GB/s (% of peak), MaxSim rerank, 1 GPU"
 SCORE_SOURCES = [
     os.path.join(ROOT, "late_interaction_reranking_amd", "csrc", f)
-    for f in ("maxsim_score.h", "maxsim_score_inst.hip", "maxsim_common.h")
+    for f in ("maxsim_score.h", "maxsim_score_inst.hip", "maxsim_common.h", "maxsim_sched.h")
 ]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "score_kernel_traffic.json")
 

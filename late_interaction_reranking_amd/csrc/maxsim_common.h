@@ -33,7 +33,7 @@ constexpr int kPlanBlock = 1024;              // plan kernels: threads per block
 constexpr int kPlanMaxBlocks = 1024;          // docs per plan block grows past 2^20 docs
 constexpr int kHistStride = 32;               // words per plan block: 28 counts, tiles lo, hi
 constexpr int kItemsPerWave = 4;              // target work items per score wave
-constexpr int kMinChunkTiles = 2;
+constexpr int kMinChunkTiles = 2;              // and at least the query tiles per register group
 
 struct Header {
     unsigned long long total_tiles;          // sum over docs of ceil(len / 16)

@@ -341,7 +341,7 @@ combine_kernel(const CombineArgs a)
     __shared__ f32x4 s_quad[kScoreWaves][kMaxQuads];  // a doc's row maxima, per wave
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-    if (wave == 0) fill_bin_tables(a.hdr, a.score_waves, tab, lane);
+    if (wave == 0) fill_bin_tables(a.hdr, a.score_waves, a.nqt, tab, lane);
     __syncthreads();
     const LaneBins L = lane_bins(tab, lane);
     const uint32_t split = tab.split_docs;

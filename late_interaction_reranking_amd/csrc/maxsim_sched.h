@@ -4,7 +4,9 @@
 // The plan kernels leave, in the workspace header, the number of docs in each tile-count
 // bin and the total tile count T; the doc descriptors sit in `desc`, bins in descending
 // order. A kernel turns that into work items:
-//   - chunk size CT = max(2, ceil(T / (kItemsPerWave * W))) tiles, W = score waves;
+//   - chunk size CT = max(2, NQT, ceil(T / (kItemsPerWave * W))) tiles, W = score
+//     waves, NQT = query tiles per register group (an item's fixed cost, the per-row
+//     maxima across lanes and their store or sum, grows with NQT);
 //   - a doc of bin b is cut into K_b = ceil(2^b / CT) chunks when 2^b > CT (else 1);
 //     chunk c covers its tiles [c nt / K_b, (c + 1) nt / K_b), never empty since
 //     nt > 2^(b-1) >= K_b;
@@ -25,12 +27,13 @@ struct BinTables {
 
 // Wave 0 of a workgroup fills the tables (lane b computes bin b, lane 0 scans the
 // bins in descending order); the caller publishes them with a barrier.
-__device__ inline void fill_bin_tables(const Header *hdr, uint32_t waves, BinTables &t, int lane)
+__device__ inline void fill_bin_tables(const Header *hdr, uint32_t waves, int nqt, BinTables &t, int lane)
 {
     const unsigned long long T = hdr->total_tiles;
     const unsigned long long per = (unsigned long long)waves * kItemsPerWave;
     unsigned long long ct = (T + per - 1) / per;
     if (ct < kMinChunkTiles) ct = kMinChunkTiles;
+    if (ct < (unsigned long long)nqt) ct = (unsigned long long)nqt;
     if (ct > (1ull << 28)) ct = 1ull << 28;  // above every bin's 2^b: no splits
     const uint32_t ct32 = (uint32_t)ct;
     if (lane < kNumBins) {

@@ -189,7 +189,7 @@ score_kernel(const ScoreArgs a)
             *reinterpret_cast<u32x4 *>(qs + r * LDQ + c * 8) = v;
         }
     }
-    if (wave == 0) fill_bin_tables(a.hdr, W, tab, lane);
+    if (wave == 0) fill_bin_tables(a.hdr, W, NQT, tab, lane);
     __syncthreads();
 
     const LaneBins L = lane_bins(tab, lane);

@@ -3,7 +3,7 @@ distributions: every doc's tiles are covered exactly once by non-empty chunks, a
 split docs and their chunks fit the workspace slots the library reserves.
 
 This mirrors the formulas the plan and score kernels use (bins by tile count, chunk
-size CT = max(2, ceil(T / (4 W))), ceil(2^b / CT) chunks per doc of bin b); the GPU
+size CT = max(2, NQT, ceil(T / (4 W))), ceil(2^b / CT) chunks per doc of bin b); the GPU
 parity tests exercise the kernels themselves.
 """
 
@@ -18,10 +18,10 @@ def bin_of(nt):
     return 0 if nt <= 1 else int(nt - 1).bit_length()
 
 
-def schedule(lengths, waves):
+def schedule(lengths, waves, nqt=1):
     nt = [(int(n) + 15) // 16 for n in lengths]
     T = sum(nt)
-    ct = max(2, -(-T // (waves * ITEMS_PER_WAVE)))
+    ct = max(2, nqt, -(-T // (waves * ITEMS_PER_WAVE)))
     bins = [[] for _ in range(NUM_BINS)]
     for i, t in enumerate(nt):
         bins[bin_of(t)].append(i)
@@ -40,7 +40,8 @@ def schedule(lengths, waves):
 
 @pytest.mark.parametrize("seed", range(12))
 @pytest.mark.parametrize("waves", [64, 1024, 8192])
-def test_schedule_covers_and_fits(seed, waves):
+@pytest.mark.parametrize("nqt", [1, 8])
+def test_schedule_covers_and_fits(seed, waves, nqt):
     rng = np.random.default_rng(seed)
     kind = seed % 4
     B = int(rng.integers(1, 3000))
@@ -52,7 +53,7 @@ def test_schedule_covers_and_fits(seed, waves):
         lengths = rng.integers(0, 3, size=B) * rng.integers(1, 40000, size=B)
     else:
         lengths = np.full(B, int(rng.integers(1, 5000)))
-    nt, items = schedule(lengths, waves)
+    nt, items = schedule(lengths, waves, nqt)
     covered = [[] for _ in lengths]
     for claim, desc, i, c, K, (a, b) in items:
         if nt[i] > 0:
