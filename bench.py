@@ -287,8 +287,8 @@ def main() -> int:
     else:
         def plan():
             lir.maxsim_plan(offs, lens, w.Lq, w.d, ws)
-    if args.short and (w.shared_docs or w.multi_query or w.X8 is not None or args.topk):
-        print("--short applies to single-query 16-bit workloads without --topk", file=sys.stderr)
+    if args.short and (w.shared_docs or w.multi_query or args.topk):
+        print("--short applies to single-query workloads without --topk", file=sys.stderr)
         return 2
     if args.topk:
         if w.shared_docs or w.multi_query:
@@ -317,7 +317,10 @@ def main() -> int:
         if args.short:
             if ev_a is not None:
                 ev_a.record()
-            lir.maxsim_rerank_short(Q, X, offs, lens, scores=scores)
+            if w.X8 is not None:
+                lir.maxsim_rerank_short_fp8(Q, X, offs, lens, w.doc_scale, scores=scores)
+            else:
+                lir.maxsim_rerank_short(Q, X, offs, lens, scores=scores)
             if ev_b is not None:
                 ev_b.record()
             return

@@ -203,6 +203,19 @@ MAXSIM_API int maxsim_rerank_fp8_bf16(const void *Q, int32_t Lq, int32_t d,
                            float doc_scale, float *scores, void *stream);
 
 /*
+ * maxsim_rerank_fp8's operation in maxsim_rerank_short's single launch (one workgroup
+ * per doc, no schedule, nothing allocated). dtype is the query format, MAXSIM_F16 or
+ * MAXSIM_BF16 (MAXSIM_ERR_INVALID_ARG otherwise). Scores are bitwise those of
+ * maxsim_rerank_fp8 (for dtype MAXSIM_BF16, maxsim_rerank_fp8_bf16); the FP8 envelope
+ * and scale checks of maxsim_rerank_fp8 and the one-register-group limit of
+ * maxsim_rerank_short apply.
+ */
+MAXSIM_API int maxsim_rerank_short_fp8(int dtype, const void *Q, int32_t Lq, int32_t d,
+                            const void *docs, int64_t stride,
+                            const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                            float doc_scale, float *scores, void *stream);
+
+/*
  * Top-k of a score array on the GPU (the rerank's consumer: the Flash-MaxSim rerank page
  * returns raw per-doc scores, `flash_maxsim_rerank_direct` return value, and the caller
  * keeps the best docs). Order: score descending; equal scores (-0 equal to +0) by

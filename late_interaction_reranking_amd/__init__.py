@@ -36,6 +36,7 @@ from .maxsim import (  # noqa: F401
     maxsim_finish,
     maxsim_finish_fp8,
     maxsim_rerank_fp8,
+    maxsim_rerank_short_fp8,
     maxsim_score,
     maxsim_score_fp8,
     maxsim_status_string,

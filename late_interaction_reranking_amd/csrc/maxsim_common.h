@@ -191,6 +191,7 @@ struct ShortArgs {
     const int32_t *lengths;   // [B]
     float *scores;            // [B]
     int32_t B, d, Lq;
+    float doc_scale;          // FP8 docs: multiplies each sum (unused otherwise)
 };
 
 // ---------------------------------------------------------------- combine kernel

@@ -44,7 +44,7 @@ MAXSIM_DECLARE_LOOKUPS(f16_fp8)
 MAXSIM_DECLARE_LOOKUPS(bf16_fp8)
 #undef MAXSIM_DECLARE_LOOKUPS
 
-// One-launch short-doc kernels, one lookup per (format, K-steps) file of 16-bit docs.
+// One-launch short-doc kernels, one lookup per (format, K-steps) file.
 #define MAXSIM_DECLARE_SHORT(fmt)                                                   \
     const void *maxsim_short_kernel_##fmt##_k1(int);                               \
     const void *maxsim_short_kernel_##fmt##_k2(int);                               \
@@ -70,6 +70,8 @@ MAXSIM_DECLARE_LOOKUPS(bf16_fp8)
     }
 MAXSIM_DECLARE_SHORT(f16)
 MAXSIM_DECLARE_SHORT(bf16)
+MAXSIM_DECLARE_SHORT(f16_fp8)
+MAXSIM_DECLARE_SHORT(bf16_fp8)
 #undef MAXSIM_DECLARE_SHORT
 
 namespace {
@@ -728,24 +730,40 @@ int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, in
     return run_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, stream);
 }
 
-// One launch, one workgroup per doc (csrc/maxsim_short.h); the query must fit one
-// register group.
-int rerank_short(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
-                 const int32_t *offsets, const int32_t *lengths, int32_t B, float *scores, void *stream_ptr)
+// Extra checks for docs stored as FP8 E4M3 bytes: whole 16-byte chunks per row and a
+// finite positive scale.
+int check_fp8(int32_t d, int64_t stride, float doc_scale)
 {
+    if (!(doc_scale > 0.0f) || doc_scale > 3.4e38f) return MAXSIM_ERR_INVALID_ARG;
+    if (d % 16 != 0 || stride % 16 != 0) return MAXSIM_ERR_UNSUPPORTED;
+    return MAXSIM_OK;
+}
+
+// One launch, one workgroup per doc (csrc/maxsim_short.h); the query must fit one
+// register group. fmt: query format, | kFmtFp8Docs for FP8 E4M3 docs with doc_scale.
+int rerank_short(int fmt, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                 const int32_t *offsets, const int32_t *lengths, int32_t B, float doc_scale, float *scores,
+                 void *stream_ptr)
+{
+    const int dtype = fmt & ~kFmtFp8Docs;
+    const bool fp8 = (fmt & kFmtFp8Docs) != 0;
     if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
-    const int st = check_common(Q, Lq, d, docs, stride, offsets, lengths, B, scores);
+    int st = check_common(Q, Lq, d, docs, stride, offsets, lengths, B, scores);
     if (st != MAXSIM_OK) return st;
+    if (fp8 && (st = check_fp8(d, stride, doc_scale)) != MAXSIM_OK) return st;
     const Config c = choose_config(Lq, d);
     if (Lq > 0 && c.ngroups != 1) return MAXSIM_ERR_UNSUPPORTED;
     if (B == 0) return MAXSIM_OK;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     if (Lq == 0) return launch_fill(scores, B, 0.0f, stream);
-    const void *fn = dtype == MAXSIM_BF16 ? maxsim_short_kernel_bf16(c.nks, c.nqt) : maxsim_short_kernel_f16(c.nks, c.nqt);
+    const void *fn = fp8 ? (dtype == MAXSIM_BF16 ? maxsim_short_kernel_bf16_fp8(c.nks, c.nqt)
+                                                 : maxsim_short_kernel_f16_fp8(c.nks, c.nqt))
+                         : (dtype == MAXSIM_BF16 ? maxsim_short_kernel_bf16(c.nks, c.nqt)
+                                                 : maxsim_short_kernel_f16(c.nks, c.nqt));
     if (!fn) return MAXSIM_ERR_UNSUPPORTED;
     // The query tile first, then the tile slots over it (the same LDS-DMA rule as the
     // scheduled kernel).
-    const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt, false) * dma_tile_bytes(c.nks, false);
+    const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt, fp8) * dma_tile_bytes(c.nks, fp8);
     const size_t lds = q_lds_bytes(c) > slots ? q_lds_bytes(c) : slots;
     int per_cu = 0;
     if (score_blocks_per_cu(fn, lds, &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
@@ -758,13 +776,14 @@ int rerank_short(int dtype, const void *Q, int32_t Lq, int32_t d, const void *do
     ShortArgs a;
     a.Q = static_cast<const uint16_t *>(Q);
     a.docs = static_cast<const char *>(docs);
-    a.stride_bytes = stride * 2;
+    a.stride_bytes = fp8 ? stride : stride * 2;
     a.offsets = offsets;
     a.lengths = lengths;
     a.scores = scores;
     a.B = B;
     a.d = d;
     a.Lq = Lq;
+    a.doc_scale = fp8 ? doc_scale : 1.0f;
     void *args[] = {&a};
     if (hipLaunchKernel(fn, dim3(grid), dim3(kScoreBlock), args, lds, stream) != hipSuccess) return MAXSIM_ERR_HIP;
     return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
@@ -799,15 +818,6 @@ int rerank_topk(int dtype, const void *Q, int32_t Lq, int32_t d, const void *doc
         rc = launch_topk(scores, B, k, top_scores, top_ids, static_cast<char *>(buf) + score_bytes, stream);
     if (hipFreeAsync(buf, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
     return rc;
-}
-
-// Extra checks for docs stored as FP8 E4M3 bytes: whole 16-byte chunks per row and a
-// finite positive scale.
-int check_fp8(int32_t d, int64_t stride, float doc_scale)
-{
-    if (!(doc_scale > 0.0f) || doc_scale > 3.4e38f) return MAXSIM_ERR_INVALID_ARG;
-    if (d % 16 != 0 || stride % 16 != 0) return MAXSIM_ERR_UNSUPPORTED;
-    return MAXSIM_OK;
 }
 
 int rerank_fp8(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
@@ -1015,7 +1025,17 @@ int maxsim_rerank_short(int dtype, const void *Q, int32_t Lq, int32_t d, const v
                         const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, float *scores,
                         void *stream)
 {
-    return rerank_short(dtype, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores, stream);
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
+    return rerank_short(dtype, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, 1.0f, scores, stream);
+}
+
+int maxsim_rerank_short_fp8(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                            const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, float doc_scale,
+                            float *scores, void *stream)
+{
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
+    return rerank_short(dtype | kFmtFp8Docs, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, doc_scale,
+                        scores, stream);
 }
 
 int maxsim_rerank_pairs(const void *Qs, int32_t q_rows, int32_t d, const int32_t *q_offsets,

@@ -1,7 +1,7 @@
 // Score kernel instances for one query format, one doc storage and one K-step count,
 // chosen by -DMAXSIM_BF16=0|1 -DMAXSIM_FP8=0|1 -DMAXSIM_NKS=1..8 (the build compiles
 // this file once per triple, in parallel). Query tiles per group NQT run 1..8 with
-// NQT * NKS <= 32. Files for 16-bit docs also hold the one-launch short-doc kernel.
+// NQT * NKS <= 32. Each file also holds the one-launch short-doc kernel of its triple.
 #include "maxsim_score.h"
 #include "maxsim_short.h"
 
@@ -38,8 +38,9 @@ constexpr int min_waves()
 template <int NQT>
 const void *short_entry()
 {
-    if constexpr (!FP8 && NQT * NKS <= maxsim::kMaxFragsPerGroup)
-        return reinterpret_cast<const void *>(&maxsim::short_kernel<NKS, NQT, BF, pipe_depth<NQT>(), min_waves<NQT>()>);
+    if constexpr (NQT * NKS <= maxsim::kMaxFragsPerGroup)
+        return reinterpret_cast<const void *>(
+            &maxsim::short_kernel<NKS, NQT, BF, FP8, pipe_depth<NQT>(), min_waves<NQT>()>);
     else
         return nullptr;
 }
@@ -83,9 +84,12 @@ const void *MAXSIM_LOOKUP(int nqt)
     }
 }
 
-#if !MAXSIM_FP8
-#if MAXSIM_BF16
+#if MAXSIM_BF16 && MAXSIM_FP8
+#define MAXSIM_SHORT_LOOKUP MAXSIM_CAT(maxsim_short_kernel_bf16_fp8_k, MAXSIM_NKS)
+#elif MAXSIM_BF16
 #define MAXSIM_SHORT_LOOKUP MAXSIM_CAT(maxsim_short_kernel_bf16_k, MAXSIM_NKS)
+#elif MAXSIM_FP8
+#define MAXSIM_SHORT_LOOKUP MAXSIM_CAT(maxsim_short_kernel_f16_fp8_k, MAXSIM_NKS)
 #else
 #define MAXSIM_SHORT_LOOKUP MAXSIM_CAT(maxsim_short_kernel_f16_k, MAXSIM_NKS)
 #endif
@@ -104,4 +108,3 @@ const void *MAXSIM_SHORT_LOOKUP(int nqt)
     default: return nullptr;
     }
 }
-#endif

@@ -14,19 +14,23 @@
 // same, so a score is bitwise the one the scheduled path gives. The query must fit one
 // register group (NQT query tiles of NKS K-steps). The time of a launch follows its
 // longest doc: long or very unequal docs belong on the scheduled path.
+//
+// FP8D: docs stored as FP8 E4M3 bytes, staged and converted to Q's format per fragment
+// as in the score kernel; the sum is multiplied by a.doc_scale after the same fixed-order
+// sum, as the scheduled path does.
 #pragma once
 
 #include "maxsim_score.h"
 
 namespace maxsim {
 
-template <int NKS, int NQT, bool BF16, int P, int MINW>
+template <int NKS, int NQT, bool BF16, bool FP8D, int P, int MINW>
 __global__ void __launch_bounds__(kScoreBlock, MINW)
 short_kernel(const ShortArgs a)
 {
     constexpr int DPAD = NKS * kStepK;
     constexpr int LDQ = DPAD + 8;                 // Q row pitch in LDS (halves), as the score kernel's
-    constexpr int CP = dma_row_chunks(NKS, false);
+    constexpr int CP = dma_row_chunks(NKS, FP8D);
     constexpr int NLDD = CP / 4;
     constexpr int TILE_CHUNKS = kTileRows * CP;
     constexpr int LQP = NQT * kTileRows;          // padded query rows
@@ -63,7 +67,7 @@ short_kernel(const ShortArgs a)
     // ---- LDS-DMA slots and fragment addresses (the score kernel's layout)
     const uint32_t stride_bytes = (uint32_t)a.stride_bytes;
     const uint32_t tile_bytes = (uint32_t)kTileRows * stride_bytes;
-    const int C = a.d / 8;
+    const int C = FP8D ? a.d / 16 : a.d / 8;  // 16-byte chunks per doc row
     u32x4 *const slots = reinterpret_cast<u32x4 *>(qs) + wave * (P * TILE_CHUNKS);
     uint32_t dma_off[NLDD];
 #pragma unroll
@@ -73,9 +77,15 @@ short_kernel(const ShortArgs a)
         const int c = (q % CP) ^ dma_swizzle(row, CP);
         dma_off[s] = c < C ? (uint32_t)row * stride_bytes + (uint32_t)c * 16u : (uint32_t)kTileRows * stride_bytes;
     }
+    // B fragment of K-step s: 16-bit docs, chunk kgroup + 4 s; FP8 docs, the 8 bytes at
+    // half kgroup % 2 of chunk kgroup / 2 + 2 s.
     int rd_dma[NKS];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) rd_dma[s] = row_in_tile * CP + ((kgroup + 4 * s) ^ dma_swizzle(row_in_tile, CP));
+    for (int s = 0; s < NKS; ++s) {
+        const int c = FP8D ? (kgroup >> 1) + 2 * s : kgroup + 4 * s;
+        rd_dma[s] = row_in_tile * CP + (c ^ dma_swizzle(row_in_tile, CP));
+    }
+    const int rd_half = (kgroup & 1) * 8;
 
     for (uint32_t doc = blockIdx.x; doc < (uint32_t)a.B; doc += gridDim.x) {
         typedef __attribute__((address_space(4))) const int32_t ConstI32;
@@ -115,7 +125,16 @@ short_kernel(const ShortArgs a)
             __builtin_amdgcn_s_waitcnt(wait_vmcnt(NLDD * (P - 1)));
             u32x4 bf[NKS];
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) bf[s] = slots[slot * TILE_CHUNKS + rd_dma[s]];
+            for (int s = 0; s < NKS; ++s) {
+                if constexpr (FP8D) {
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    const u32x2 v = *reinterpret_cast<const u32x2 *>(
+                        reinterpret_cast<const char *>(slots + slot * TILE_CHUNKS + rd_dma[s]) + rd_half);
+                    bf[s] = e4m3x8_to_16<BF16>(v[0], v[1]);
+                } else {
+                    bf[s] = slots[slot * TILE_CHUNKS + rd_dma[s]];
+                }
+            }
             const float c0 = row_in_tile < left ? 0.0f : NEG_INF;
             // Tile qt's products in one accumulator while tile qt - 1's are folded into
             // the running max (as in the score kernel).
@@ -188,7 +207,9 @@ short_kernel(const ShortArgs a)
             const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 16));
             const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 32));
             const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
-            if (lane == 0) a.scores[doc] = ((s0 + s1) + s2) + s3;
+            float sum = ((s0 + s1) + s2) + s3;
+            if constexpr (FP8D) sum *= a.doc_scale;
+            if (lane == 0) a.scores[doc] = sum;
         }
         __syncthreads();  // part is reused by the next doc
     }

@@ -26,6 +26,7 @@ The functions carry the C ABI's names (include/maxsim.h) and take torch tensors:
 
     maxsim_rerank_fp8(Q, docs8, doc_offsets, doc_lengths, doc_scale)
                        FP8 E4M3 docs (uint8 or float8_e4m3fn), fp16 or bf16 Q
+    maxsim_rerank_short_fp8(...)  the same in one launch, one workgroup per doc
     maxsim_score_fp8(...), maxsim_finish_fp8(...)   staged form, after maxsim_plan
 
     maxsim_rerank_pairs_fp8(Qs, ..., doc_query, doc_scale)      pairs over FP8 docs
@@ -72,6 +73,7 @@ __all__ = [
     "maxsim_rerank_multi_bf16",
     "rerank_multi",
     "maxsim_rerank_fp8",
+    "maxsim_rerank_short_fp8",
     "maxsim_score_fp8",
     "maxsim_finish_fp8",
     "maxsim_topk",
@@ -146,6 +148,8 @@ def load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = ctypes.c_int
             fn.argtypes = [P, I32, I32, P, I64, P, P, I32, F32, P, P]
+        lib.maxsim_rerank_short_fp8.restype = ctypes.c_int
+        lib.maxsim_rerank_short_fp8.argtypes = [ctypes.c_int, P, I32, I32, P, I64, P, P, I32, F32, P, P]
         lib.maxsim_score_fp8.restype = ctypes.c_int
         lib.maxsim_score_fp8.argtypes = [ctypes.c_int, P, I32, I32, P, I64, P, P, I32, F32, P, P, SZ, P]
         lib.maxsim_finish_fp8.restype = ctypes.c_int
@@ -483,6 +487,23 @@ def maxsim_rerank_fp8(Q, docs, doc_offsets, doc_lengths, doc_scale: float, score
                                    doc_lengths.data_ptr(), B, float(doc_scale), scores.data_ptr(),
                                    _stream(docs))
     _check(st, name)
+    return scores
+
+
+def maxsim_rerank_short_fp8(Q, docs, doc_offsets, doc_lengths, doc_scale: float, scores=None) -> torch.Tensor:
+    """maxsim_rerank_fp8's scores in one launch, one workgroup per doc (for batches of
+    short docs); bitwise equal to maxsim_rerank_fp8 with the same query dtype."""
+    Lq, d, stride, B = _check_fp8_args(Q, docs, doc_offsets, doc_lengths)
+    if scores is None:
+        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
+    elif scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
+        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    code = MAXSIM_BF16 if Q.dtype == torch.bfloat16 else MAXSIM_F16
+    with torch.cuda.device(docs.device):
+        st = load().maxsim_rerank_short_fp8(code, Q.data_ptr(), Lq, d, docs.data_ptr(), stride,
+                                            doc_offsets.data_ptr(), doc_lengths.data_ptr(), B,
+                                            float(doc_scale), scores.data_ptr(), _stream(docs))
+    _check(st, "maxsim_rerank_short_fp8")
     return scores
 
 

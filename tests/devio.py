@@ -26,6 +26,16 @@ def upload(w, dev=DEV):
     return Q, X, offs, lens
 
 
+def upload8(w, dev=DEV):
+    """(Q, FP8 doc bytes [T, d] with the workload's byte stride, offsets, lengths)."""
+    t = tdtype(w.dtype)
+    Q = torch.from_numpy(np.ascontiguousarray(w.Q).view(np.int16)).to(dev).view(t)
+    X8 = torch.from_numpy(w.X8).to(dev)[:, : w.d]
+    offs = torch.from_numpy(np.ascontiguousarray(w.offsets, dtype=np.int32)).to(dev)
+    lens = torch.from_numpy(np.ascontiguousarray(w.lengths, dtype=np.int32)).to(dev)
+    return Q, X8, offs, lens
+
+
 def gpu_scores(w, dev=DEV) -> np.ndarray:
     Q, X, offs, lens = upload(w, dev)
     s = lir.rerank(Q, X, offs, lens)

@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
               "maxsim_plan_pairs", "maxsim_rerank_multi", "maxsim_rerank_multi_bf16",
               "maxsim_rerank_fp8", "maxsim_rerank_fp8_bf16", "maxsim_score_fp8", "maxsim_finish_fp8",
               "maxsim_topk_workspace_size", "maxsim_topk", "maxsim_rerank_topk", "maxsim_rerank_topk_bf16",
-              "maxsim_rerank_pairs_fp8", "maxsim_rerank_multi_fp8", "maxsim_rerank_short"):
+              "maxsim_rerank_pairs_fp8", "maxsim_rerank_multi_fp8", "maxsim_rerank_short",
+              "maxsim_rerank_short_fp8"):
         assert n in names
 
 
@@ -123,6 +124,37 @@ def call_short(lib, dtype=0, **kw):
 ])
 def test_short_validation(lib, kw, code):
     assert call_short(lib, **kw) == code
+
+
+def call_short_fp8(lib, dtype=0, scale=1.0, **kw):
+    args = dict(Q=FAKE, Lq=32, d=128, docs=FAKE, stride=128, offs=FAKE, lens=FAKE + 1024, B=10,
+                scores=FAKE + 4096)
+    args.update(kw)
+    fn = lib.maxsim_rerank_short_fp8
+    fn.argtypes = [ctypes.c_int, ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p,
+                   ctypes.c_int64, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    return fn(dtype, args["Q"], args["Lq"], args["d"], args["docs"], args["stride"], args["offs"],
+              args["lens"], args["B"], scale, args["scores"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), INVALID),                        # a format flag is not a query format
+    (dict(dtype=3), INVALID),
+    (dict(scale=0.0), INVALID),
+    (dict(scale=-1.0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("inf")), INVALID),
+    (dict(d=24, stride=32), UNSUPPORTED),            # d % 16
+    (dict(stride=136), UNSUPPORTED),                 # stride % 16 (bytes)
+    (dict(Lq=129, d=128), UNSUPPORTED),              # more than one register group
+    (dict(B=-1), INVALID),
+    (dict(docs=None), INVALID),
+    (dict(B=0, docs=None, offs=None, lens=None, scores=None), OK),
+    (dict(dtype=1, B=0, docs=None, offs=None, lens=None, scores=None), OK),
+])
+def test_short_fp8_validation(lib, kw, code):
+    assert call_short_fp8(lib, **kw) == code
 
 
 def test_staged_validation(lib):

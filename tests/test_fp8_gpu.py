@@ -17,20 +17,11 @@ torch = pytest.importorskip("torch")
 
 if torch.cuda.is_available():
     import late_interaction_reranking_amd as lir
-    from devio import DEV, assert_parity, gpu_scores, tdtype
+    from devio import DEV, assert_parity, gpu_scores, upload8
 
 
 def _say(msg):
     print(msg, flush=True)
-
-
-def upload8(w):
-    t = tdtype(w.dtype)
-    Q = torch.from_numpy(np.ascontiguousarray(w.Q).view(np.int16)).to(DEV).view(t)
-    X8 = torch.from_numpy(w.X8).to(DEV)[:, : w.d]
-    offs = torch.from_numpy(np.ascontiguousarray(w.offsets, dtype=np.int32)).to(DEV)
-    lens = torch.from_numpy(np.ascontiguousarray(w.lengths, dtype=np.int32)).to(DEV)
-    return Q, X8, offs, lens
 
 
 def fp8_scores(w, staged=False):

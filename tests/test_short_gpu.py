@@ -16,7 +16,7 @@ torch = pytest.importorskip("torch")
 
 if torch.cuda.is_available():
     import late_interaction_reranking_amd as lir
-    from devio import assert_parity, top10_ok, top_k, upload
+    from devio import assert_parity, top10_ok, top_k, upload, upload8
 
 
 def _say(msg):
@@ -124,3 +124,101 @@ def test_graph_capture_and_replay():
         ref = lir.rerank(Q, X, offs, lens)
         torch.cuda.synchronize()
         assert torch.equal(out, ref), f"replay {it}"
+
+
+# ------------------------------------------------------------------ FP8 E4M3 docs
+
+
+def _both8(w):
+    Q, X8, offs, lens = upload8(w)
+    short = lir.maxsim_rerank_short_fp8(Q, X8, offs, lens, w.doc_scale)
+    sched = lir.maxsim_rerank_fp8(Q, X8, offs, lens, w.doc_scale)
+    torch.cuda.synchronize()
+    return short.cpu().numpy().astype(np.float64), sched.cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("name", ["tiny", "colbert", "long_doc", "scattered"])
+def test_fp8_named_workloads(name):
+    _say(f"[short fp8] workload {name}")
+    w = workloads.to_fp8(workloads.make(name), doc_scale=1 / 300)
+    got, sched = _both8(w)
+    assert_parity(got, oracle.maxsim_workload(w), name)
+    assert np.array_equal(got, sched), name
+
+
+FP8_SHAPES = [
+    # (Lq, d, row stride in bytes): one register group, d % 16 == 0
+    (1, 128, 128), (32, 16, 16), (7, 32, 48), (37, 48, 64), (32, 128, 128), (128, 128, 144),
+    (64, 256, 256), (17, 160, 176), (96, 64, 80), (45, 208, 224),
+]
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+@pytest.mark.parametrize("Lq,d,stride8", FP8_SHAPES)
+def test_fp8_shapes_ragged(fmt, Lq, d, stride8):
+    _say(f"[short fp8] shape Lq={Lq} d={d} stride={stride8} {fmt}")
+    rng = np.random.default_rng([Lq, d, stride8, 9])
+    lengths = rng.integers(0, 120, size=60)
+    lengths[:10] = [0, 1, 15, 16, 17, 31, 32, 33, 63, 65]
+    w = workloads.custom(Lq, d, lengths, dtype=fmt, seed=Lq + 3 * d, order="shuffled", gap=(0, 5),
+                         gap_fill="nan")
+    workloads.to_fp8(w, doc_scale=0.0123, stride8=stride8)
+    got, sched = _both8(w)
+    assert_parity(got, oracle.maxsim_workload(w), f"Lq={Lq} d={d} {fmt}")
+    assert np.array_equal(got, sched)
+
+
+FINITE = np.array([b for b in range(256) if b not in (0x7F, 0xFF)], np.uint8)
+
+
+@pytest.mark.parametrize("fmt", ["f16", "bf16"])
+def test_fp8_one_hot_every_byte_exact(fmt):
+    """One-hot query rows pick single E4M3 values, so every score is exact: equal to the
+    oracle's bit for bit (every finite byte appears in some doc row)."""
+    _say(f"[short fp8] one-hot all bytes {fmt}")
+    rng = np.random.default_rng([5, len(fmt)])
+    Lq, d = 6, 64
+    lengths = rng.integers(0, 40, size=80)
+    lengths[:3] = [0, 1, 17]
+    w = workloads.custom(Lq, d, lengths, dtype=fmt, seed=5, order="shuffled", gap=(0, 3), gap_fill="nan")
+    workloads.to_fp8(w, doc_scale=1.0, stride8=d + 16)
+    for o_, n in zip(w.offsets, w.lengths):
+        w.X8[o_:o_ + n, :d] = rng.choice(FINITE, size=(n, d))
+    o0 = int(w.offsets[np.argmax(w.lengths)])
+    flat = w.X8[o0:o0 + int(w.lengths.max()), :d].reshape(-1)
+    flat[: FINITE.size] = FINITE
+    w.X8[o0:o0 + int(w.lengths.max()), :d] = flat.reshape(-1, d)
+    a = rng.integers(0, d, size=Lq)
+    w.Q = np.zeros((Lq, d), np.uint16)
+    w.Q[np.arange(Lq), a] = 0x3C00 if fmt == "f16" else 0x3F80
+    got, sched = _both8(w)
+    assert np.array_equal(got, oracle.maxsim_workload(w))
+    assert np.array_equal(got, sched)
+
+
+def test_fp8_errors_and_empty():
+    w = workloads.to_fp8(workloads.custom(32, 128, [5, 0, 9], seed=1), doc_scale=0.5)
+    Q, X8, offs, lens = upload8(w)
+    assert lir.maxsim_rerank_short_fp8(Q[:0], X8, offs, lens, 0.5).cpu().tolist() == [0.0, 0.0, 0.0]
+    assert lir.maxsim_rerank_short_fp8(Q, X8, offs[:0], lens[:0], 0.5).numel() == 0
+    with pytest.raises(lir.MaxSimError):
+        lir.maxsim_rerank_short_fp8(Q, X8, offs, lens, 0.0)
+    Q129 = torch.zeros((129, 128), dtype=torch.float16, device=Q.device)
+    with pytest.raises(lir.MaxSimError):
+        lir.maxsim_rerank_short_fp8(Q129, X8, offs, lens, 0.5)
+    with pytest.raises(TypeError):
+        lir.maxsim_rerank_short_fp8(Q, X8.to(torch.float16), offs, lens, 0.5)
+    torch.cuda.synchronize()
+
+
+@pytest.mark.slow
+def test_fp8_large_sampled():
+    """The FP8 rerank workload at full size (80,000 docs of 64 to 448 rows, offsets past
+    2**31 bytes) in one launch."""
+    _say("[short fp8] large_fp8 (generating)")
+    w = workloads.make("large_fp8")
+    got, sched = _both8(w)
+    assert np.array_equal(got, sched)
+    rng = np.random.default_rng(1)
+    sample = np.unique(np.concatenate([w.planted, rng.choice(w.B, 2000, replace=False), [0, w.B - 1]]))
+    assert_parity(got[sample], oracle.maxsim_workload(w, docs=sample), "large_fp8 (sample)")
