@@ -123,6 +123,10 @@ plan_count_kernel(const int32_t *__restrict__ lengths, int32_t B, uint32_t docs_
 
 // With a single plan block (B <= kPlanBlock docs), the scatter kernel counts its own
 // docs (self_count) and the count kernel is not launched.
+//
+// The kernel is a chain of dependent memory round trips on a small grid, so it issues
+// its first round's length, offset and query loads at entry, where they overlap the
+// histogram sums, and each round prefetches the next one's.
 __global__ void __launch_bounds__(kPlanBlock)
 plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restrict__ lengths,
                     int32_t B, uint32_t docs_per_block, const uint32_t *__restrict__ hist,
@@ -134,19 +138,37 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
     __shared__ uint32_t part_before[kRowGroups][kHistStride];
     __shared__ uint32_t bin_next[kNumBins];  // next free slot of each bin for this block
     __shared__ uint32_t wave_cnt[kPlanBlock / kWave][kNumBins];
+    __shared__ uint32_t used_bins;           // bit b: some doc of the batch is in bin b
+
+    const int64_t first = (int64_t)blockIdx.x * docs_per_block;
+    const int64_t last = first + docs_per_block < (int64_t)B ? first + docs_per_block : (int64_t)B;
+    struct DocIn {
+        int32_t len, off, q;
+    };
+    auto load_doc = [&](int64_t i) {
+        DocIn v{0, 0, 0};
+        if (i < last) {
+            v.len = lengths[i];
+            v.off = offsets[i];
+            v.q = qt.doc_query ? qt.doc_query[i] : 0;
+        }
+        return v;
+    };
+    DocIn cur = load_doc(first + threadIdx.x);
 
     if (self_count) {
-        // One block holds every doc: bin counts and tile total straight from lengths.
+        // One block holds every doc (first = 0, last = B <= kPlanBlock): bin counts and
+        // tile total straight from the lengths already loaded.
         if (threadIdx.x < kHistStride) {
             part_tot[0][threadIdx.x] = 0;
             part_before[0][threadIdx.x] = 0;
         }
         __syncthreads();
         unsigned long long my_tiles = 0;
-        for (int64_t i = threadIdx.x; i < (int64_t)B; i += kPlanBlock) {
-            const uint32_t nt = tiles_of(lengths[i]);
+        if ((int64_t)threadIdx.x < last) {
+            const uint32_t nt = tiles_of(cur.len);
             atomicAdd(&part_tot[0][bin_of(nt)], 1ull);
-            my_tiles += nt;
+            my_tiles = nt;
         }
         for (int o = 32; o > 0; o >>= 1) my_tiles += __shfl_xor(my_tiles, o);
         if ((threadIdx.x & (kWave - 1)) == 0) atomicAdd(&part_tot[0][kNumBins], my_tiles);
@@ -158,6 +180,7 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
         const int rg = threadIdx.x / kHistStride;
         unsigned long long tot = 0;
         uint32_t before = 0;
+#pragma unroll 4
         for (uint32_t k = rg; k < nblocks; k += kRowGroups) {
             const uint32_t v = hist[(size_t)k * kHistStride + c];
             tot += v;
@@ -182,10 +205,13 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
     }
     if (threadIdx.x == 0) {
         uint32_t start = 0;  // bins in descending order
+        uint32_t used = 0;
         for (int b = kNumBins - 1; b >= 0; --b) {
             bin_next[b] = start + part_before[0][b];
             start += (uint32_t)part_tot[0][b];
+            if (part_tot[0][b] != 0) used |= 1u << b;
         }
+        used_bins = used;
         if (blockIdx.x == 0) {
             for (int b = 0; b < kNumBins; ++b) hdr->bin_count[b] = (uint32_t)part_tot[0][b];
             hdr->total_tiles = part_tot[0][kNumBins] + (part_tot[0][kNumBins + 1] << 32);
@@ -195,20 +221,23 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
     __syncthreads();
 
     // Stable placement: rounds of kPlanBlock consecutive docs; inside a round, rank by
-    // (wave, lane) with one ballot per bin.
+    // (wave, lane) with one ballot per bin that holds docs of the batch (the others
+    // hold none of this block's docs either, and their counts are never read).
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = threadIdx.x / kWave;
     const unsigned long long lanes_below = (1ull << lane) - 1ull;
-    const int64_t first = (int64_t)blockIdx.x * docs_per_block;
-    const int64_t last = first + docs_per_block < (int64_t)B ? first + docs_per_block : (int64_t)B;
+    const uint32_t used = used_bins;
     for (int64_t base = first; base < last; base += kPlanBlock) {
         const int64_t i = base + threadIdx.x;
         const bool valid = i < last;
-        const int32_t len = valid ? lengths[i] : 0;
+        const DocIn in = cur;
+        cur = load_doc(i + kPlanBlock);  // the next round's docs, in flight meanwhile
+        const int32_t len = in.len;
         const uint32_t nt = tiles_of(len);
         const int bin = valid ? bin_of(nt) : -1;
         uint32_t rank = 0;
-        for (int b = 0; b < kNumBins; ++b) {
+        for (uint32_t m_bins = used; m_bins != 0u; m_bins &= m_bins - 1u) {
+            const int b = __builtin_ctz(m_bins);
             const unsigned long long m = __ballot(bin == b);
             if (lane == 0) wave_cnt[wave][b] = (uint32_t)__popcll(m);
             if (bin == b) rank = (uint32_t)__popcll(m & lanes_below);
@@ -219,13 +248,13 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
             for (int w = 0; w < wave; ++w) slot += wave_cnt[w][bin];
             DocDesc dd;
             dd.doc = (int32_t)i;
-            dd.offset = offsets[i];
+            dd.offset = in.off;
             dd.length = len > 0 ? len : 0;
             dd.tiles = (int32_t)nt;
             // The doc's query, checked here once so the score kernel needs no host
             // check: an index outside [0, nq), rows outside Q or a query longer than
             // the launch was built for make the doc's score NaN.
-            const int32_t q = qt.doc_query ? qt.doc_query[i] : 0;
+            const int32_t q = in.q;
             int32_t q_off = 0, q_len = -1;
             if (q >= 0 && q < qt.nq) {
                 q_off = qt.q_offsets ? qt.q_offsets[q] : 0;
@@ -242,7 +271,7 @@ plan_scatter_kernel(const int32_t *__restrict__ offsets, const int32_t *__restri
             desc[slot] = dd;
         }
         __syncthreads();
-        if (threadIdx.x < kNumBins) {
+        if (threadIdx.x < kNumBins && ((used >> threadIdx.x) & 1u)) {
             uint32_t add = 0;
             for (int w = 0; w < kPlanBlock / kWave; ++w) add += wave_cnt[w][threadIdx.x];
             bin_next[threadIdx.x] += add;
