@@ -146,6 +146,19 @@ __device__ __forceinline__ u32x4 e4m3x8_to_16(uint32_t lo, uint32_t hi)
     return r;
 }
 
+// Issue priority from a wave's progress through its share of the static deal: a wave
+// that has started fewer of its rounds issues first. The SIMD arbiter otherwise favours
+// the oldest waves, so the last workgroup placed on a CU would finish its equal share
+// last; this feeds back toward all waves ending together.
+__device__ __forceinline__ void progress_priority(uint32_t started, uint32_t rounds)
+{
+    const uint32_t q = rounds ? (4u * started) / rounds : 3u;
+    if (q == 0u) __builtin_amdgcn_s_setprio(3);
+    else if (q == 1u) __builtin_amdgcn_s_setprio(2);
+    else if (q == 2u) __builtin_amdgcn_s_setprio(1);
+    else __builtin_amdgcn_s_setprio(0);
+}
+
 // MINW: waves per SIMD the register allocation must allow (512 / MINW registers).
 // BF16: element format of Q (and of the MFMA). FP8D: docs stored as FP8 E4M3 bytes
 // (converted to Q's format per fragment; the score is multiplied by a.doc_scale).
@@ -414,10 +427,13 @@ score_kernel(const ScoreArgs a)
     // next query group, or the next item).
     int grp = 0;
     float lane_sum = 0.0f;
+    // Rounds of the static deal: every wave gets about `rounds` items.
+    const uint32_t rounds = (total + W - 1u) / W;
     while (wave_uniform(cur.valid ? 1u : 0u)) {
         if (grp == 0) {
             g2 = claim_of(r++);
             fetch(g2, i2, d2);
+            progress_priority(r, rounds);
         }
         if (ngroups > 1 || cur.query != loaded_query) {
             load_q(grp, cur.q_off, cur.q_len);
