@@ -19,8 +19,13 @@ query that scores it. --workload large_fp8 times the large workload with docs st
 FP8 E4M3 bytes (scale 2^-8; maxsim_plan, maxsim_score_fp8, maxsim_finish_fp8), and
 --workload shared_fp8 the shared workload with FP8 docs (maxsim_rerank_multi_fp8).
 
+After the timed steps, unless --no-read-probe, the doc tensor is read once more by a
+plain streaming read kernel (libmaxsim_probe.so, LDS-DMA and register loads) and the
+rates are reported as read_ceiling: the read bandwidth this device actually sustains,
+next to the published 8 TB/s that roofline.peak uses.
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload large]
-                    [--no-cpu-baseline] [--copy-probe]
+                    [--no-cpu-baseline] [--no-read-probe] [--copy-probe]
 """
 
 from __future__ import annotations
@@ -70,6 +75,48 @@ def measured_traffic(workload: str):
     if not ent or ent.get("score_source_digest") != score_source_digest():
         return None
     return ent.get("hbm_bytes_per_launch")
+
+
+PROBE_LIBRARY = os.path.join(ROOT, "late_interaction_reranking_amd", "libmaxsim_probe.so")
+
+
+def read_ceiling(buf, reps: int = 5):
+    """The device's plain streaming read rate over `buf` (the doc tensor, already in HBM):
+    libmaxsim_probe.so reads it once per launch with LDS-DMA loads (the score kernel's
+    tile path, nothing consumed) and with register loads; GB/s from HIP events around
+    each launch on torch's current stream, averaged over `reps` launches after one
+    warm-up."""
+    import ctypes
+
+    import torch  # before the library: it must bind to torch's HIP runtime (same soname)
+
+    lib = ctypes.CDLL(PROBE_LIBRARY)
+    lib.maxsim_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    blocks = int(lib.maxsim_probe_blocks())
+    if blocks < 1:
+        raise RuntimeError("maxsim_probe_blocks failed")
+    base = buf if buf._base is None else buf._base
+    nbytes = base.numel() * base.element_size()
+    nbytes -= nbytes % 16
+    sink = torch.empty(blocks * 256, dtype=torch.int32, device=base.device)
+    stream = torch.cuda.current_stream().cuda_stream
+    out = {"kernel": "libmaxsim_probe.so: probe_lds_kernel, probe_reg_kernel", "bytes": nbytes,
+           "blocks": blocks, "launches": reps}
+    for mode, key in ((0, "lds_dma_GBps"), (1, "register_GBps")):
+        ms = []
+        for i in range(reps + 1):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            rc = lib.maxsim_probe_read(base.data_ptr(), nbytes, mode, blocks, sink.data_ptr(), stream)
+            b.record()
+            if rc != 0:
+                raise RuntimeError(f"maxsim_probe_read returned {rc}")
+            torch.cuda.synchronize()
+            if i > 0:
+                ms.append(a.elapsed_time(b))
+        out[key] = nbytes / (sum(ms) / len(ms) * 1e-3) / 1e9
+    return out
 
 
 def algorithmic_bytes(w) -> int:
@@ -237,6 +284,9 @@ def main() -> int:
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of one step captured in a HIP graph (no host "
                          "launch cost per kernel); the per-launch roofline still comes from eager steps")
+    ap.add_argument("--no-read-probe", action="store_true",
+                    help="skip the read-ceiling probe (a plain streaming read of the doc tensor, "
+                         "reported as read_ceiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one plain 2 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -400,6 +450,12 @@ def main() -> int:
         log("copy probe: one device copy of 2 GiB (reads 2 GiB, writes 2 GiB)")
         del src, dst
 
+    ceiling = None
+    if not args.no_read_probe:
+        ceiling = read_ceiling(X)
+        log(f"read ceiling over {ceiling['bytes']} bytes: LDS-DMA {ceiling['lds_dma_GBps']:.0f} GB/s, "
+            f"registers {ceiling['register_GBps']:.0f} GB/s")
+
     alg_bytes = algorithmic_bytes(w)
     launches = score_launches(w)
     # Per score launch: one maxsim_rerank_multi call holds `launches` score launches, each
@@ -460,6 +516,9 @@ def main() -> int:
         "cpu_baseline": None,
         "parity": None,
     }
+    if ceiling is not None:
+        ceiling["score_frac_of_ceiling"] = achieved / max(ceiling["lds_dma_GBps"], ceiling["register_GBps"])
+        rec["read_ceiling"] = ceiling
     if args.topk:
         tk_ms = [a.elapsed_time(b) for a, b in tk_events]
         rec["topk"] = {"k": args.topk, "avg_ms": sum(tk_ms) / len(tk_ms), "included_in_step": True}
