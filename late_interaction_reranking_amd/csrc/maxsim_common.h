@@ -33,6 +33,7 @@ constexpr int kPlanBlock = 1024;              // plan kernels: threads per block
 constexpr int kPlanMaxBlocks = 1024;          // docs per plan block grows past 2^20 docs
 constexpr int kHistStride = 32;               // words per plan block: 28 counts, tiles lo, hi
 constexpr int kItemsPerWave = 4;              // target work items per score wave
+constexpr uint32_t kDealPeriod = 12;          // deal rounds per period; odd-XCD waves sit out one
 constexpr int kMinChunkTiles = 2;              // and at least the query tiles per register group
 
 struct Header {
