@@ -4,8 +4,12 @@
 // the rerank library: built as libmaxsim_probe.so and loaded by the benchmark only.
 //
 // Both modes read 1 KB of consecutive bytes per wave instruction (16 bytes per lane),
-// non-temporal, over a persistent grid of workgroups of 4 waves. Wave w of W reads the
-// 4 KB tiles [w T / W, (w + 1) T / W) of the T = ceil(bytes / 4096) tiles.
+// non-temporal, over a persistent grid of workgroups of 4 waves. Wave w reads the 4 KB
+// tiles [T c(w) / c(W), T c(w + 1) / c(W)) of the T = ceil(bytes / 4096) tiles, c being
+// the running sum of the waves' weights. Workgroups sit on the eight XCDs round robin
+// (block b on XCD b % 8) and the odd-numbered XCDs read ~8 % slower, so when the grid
+// is a multiple of 8 blocks a wave of an odd block weighs 11 and one of an even block 12
+// (the split the score kernel's deal also makes); otherwise every wave weighs 1.
 //   - mode 0, LDS-DMA: buffer_load_dwordx4 ... lds into 3 tile slots per wave, as the
 //     score kernel loads its 16-bit doc tiles (at 3 workgroups per CU, the score kernel's
 //     own occupancy on a 128-column query of 32 rows); nothing reads the tiles.
@@ -43,6 +47,20 @@ __device__ __forceinline__ uint64_t uniform64(uint64_t v)
     return (uint64_t)uniform32((uint32_t)v) | ((uint64_t)uniform32((uint32_t)(v >> 32)) << 32);
 }
 
+// Running sum of the weights of waves [0, v).
+__device__ __forceinline__ uint64_t weight_before(uint64_t v, bool weighted)
+{
+    if (!weighted) return v;
+    const uint64_t pairs = v / (2 * kWaves), r = v % (2 * kWaves);  // an even block, then an odd one
+    return pairs * (kWaves * 12 + kWaves * 11) + (r < kWaves ? r * 12 : kWaves * 12 + (r - kWaves) * 11);
+}
+
+__device__ __forceinline__ uint64_t first_tile(uint64_t v, uint64_t W, uint64_t T)
+{
+    const bool weighted = (gridDim.x & 7u) == 0u;
+    return T * weight_before(v, weighted) / weight_before(W, weighted);
+}
+
 __global__ void __launch_bounds__(kBlock) probe_lds_kernel(const char *buf, uint64_t bytes, uint32_t *sink)
 {
     __shared__ __attribute__((aligned(16))) u32x4 slots[kWaves * kSlots * kTile / 16];
@@ -51,8 +69,8 @@ __global__ void __launch_bounds__(kBlock) probe_lds_kernel(const char *buf, uint
     const uint64_t W = (uint64_t)gridDim.x * kWaves;
     const uint64_t wid = (uint64_t)blockIdx.x * kWaves + wave;
     const uint64_t T = (bytes + kTile - 1) / kTile;
-    const uint64_t t0 = uniform64(wid * T / W);
-    const uint64_t t1 = uniform64((wid + 1) * T / W);
+    const uint64_t t0 = uniform64(first_tile(wid, W, T));
+    const uint64_t t1 = uniform64(first_tile(wid + 1, W, T));
     u32x4 *const mine = slots + wave * (kSlots * kTile / 16);
 
     // Loads of tile t into slot `slot`; a tile past the wave's range loads nothing (its
@@ -103,8 +121,8 @@ __global__ void __launch_bounds__(kBlock) probe_reg_kernel(const char *buf, uint
     const uint64_t W = (uint64_t)gridDim.x * kWaves;
     const uint64_t wid = (uint64_t)blockIdx.x * kWaves + wave;
     const uint64_t T = (bytes + kTile - 1) / kTile;
-    const uint64_t t0 = uniform64(wid * T / W);
-    const uint64_t t1 = uniform64((wid + 1) * T / W);
+    const uint64_t t0 = uniform64(first_tile(wid, W, T));
+    const uint64_t t1 = uniform64(first_tile(wid + 1, W, T));
     u32x4 acc = {0u, 0u, 0u, 0u};
     // Whole tiles in groups of kGroup, loads first and xors after, so that the group's
     // 16 loads are in flight together; then single whole tiles; then the buffer's partial

@@ -53,14 +53,21 @@ def test_rejects_bad_arguments_on_the_host(buf, nbytes, mode, blocks, sink):
 
 def expected_register_sink(data: np.ndarray, blocks: int) -> np.ndarray:
     """Per lane of every wave: the xor of the four words of every 16-byte chunk the
-    register mode gives it (wave w: tiles [w T / W, (w + 1) T / W); lane l: the chunks at
+    register mode gives it (wave w: tiles [T c(w) / c(W), T c(w + 1) / c(W)), c the
+    running sum of wave weights: 12 for a wave of an even block and 11 for one of an odd
+    block when the grid is a multiple of 8 blocks, else 1; lane l: the chunks at
     l + 64 s, s < 4, of each tile that lie inside the buffer)."""
     nbytes = data.size
     words = data.view(np.uint32).reshape(-1, 4)
     chunk_fold = words[:, 0] ^ words[:, 1] ^ words[:, 2] ^ words[:, 3]
     W = blocks * WAVES
     T = (nbytes + TILE - 1) // TILE
-    starts = np.arange(W + 1, dtype=np.int64) * T // W
+    if blocks % 8 == 0:
+        weight = np.where((np.arange(W) // WAVES) % 2 == 0, 12, 11).astype(np.int64)
+    else:
+        weight = np.ones(W, dtype=np.int64)
+    cum = np.concatenate([[0], np.cumsum(weight)])
+    starts = T * cum // cum[-1]
     c = np.arange(chunk_fold.size, dtype=np.int64)
     tile = c * 16 // TILE
     e = c % (TILE // 16)
