@@ -24,8 +24,20 @@ plain streaming read kernel (libmaxsim_probe.so, LDS-DMA and register loads) and
 rates are reported as read_ceiling: the read bandwidth this device actually sustains,
 next to the published 8 TB/s that roofline.peak uses.
 
+Cache eviction (flushed): after the K back-to-back steps that give `value`, each of
+--flush-reps further steps runs right after a 1 GiB write that evicts the 256 MB MALL
+and the L2s (outside the events); the write also keeps the GPU busy while the host
+enqueues the step, so these events time the step's kernels and the gaps between them,
+not the host's launch cost. `flushed` reports their median, p10 and p90, and those of
+the score kernel alone.
+
+--one-shot also times the one-shot entry point (maxsim_rerank, maxsim_rerank_fp8 or
+maxsim_rerank_pairs) with a synchronise after every call, host wall clock per call,
+against the staged path (plan, score, finish on a caller workspace) timed the same way.
+
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload large]
                     [--no-cpu-baseline] [--no-read-probe] [--copy-probe]
+                    [--flush-reps N] [--one-shot]
 """
 
 from __future__ import annotations
@@ -164,15 +176,59 @@ def score_launches(w) -> int:
     return passes + (1 if cur else 0)
 
 
-def cpu_model() -> str:
+def cpu_info() -> dict:
+    """The host CPU as /proc/cpuinfo names it (the full model string, vendor, family,
+    model, logical CPUs listed) and the CPUs this process may run on."""
+    info = {"model_name": "unknown"}
     try:
         with open("/proc/cpuinfo") as fh:
-            for line in fh:
-                if line.startswith("model name"):
-                    return line.split(":", 1)[1].strip()
+            text = fh.read()
+        first = text.split("\n\n", 1)[0]
+        for line in first.splitlines():
+            if ":" not in line:
+                continue
+            k, v = (x.strip() for x in line.split(":", 1))
+            if k == "model name":
+                info["model_name"] = v
+            elif k in ("vendor_id", "cpu family", "model", "stepping", "cpu MHz", "cache size"):
+                info[k.replace(" ", "_")] = v
+        info["logical_cpus_listed"] = text.count("processor\t:")
     except OSError:
         pass
-    return "unknown"
+    info["affinity_cpus"] = len(os.sched_getaffinity(0))
+    info["os_cpu_count"] = os.cpu_count()
+    quota = cgroup_cpu_quota()
+    if quota is not None:
+        info["cgroup_cpu_quota"] = quota
+    if os.environ.get("OMP_NUM_THREADS"):
+        info["OMP_NUM_THREADS"] = os.environ["OMP_NUM_THREADS"]
+    return info
+
+
+def cgroup_cpu_quota():
+    """CPUs' worth of time the process's cgroup may use (cgroup v2 cpu.max), or None."""
+    try:
+        with open("/sys/fs/cgroup/cpu.max") as fh:
+            quota, period = fh.read().split()[:2]
+        if quota == "max":
+            return None
+        return float(quota) / float(period)
+    except (OSError, ValueError):
+        return None
+
+
+def host_threads() -> int:
+    """Threads for the oracle: every CPU this process may run on (its affinity mask),
+    but no more than its CPU share where one is set (a cgroup quota, or the machine's
+    OMP_NUM_THREADS): threads beyond the share would only queue for the same time."""
+    n = len(os.sched_getaffinity(0))
+    quota = cgroup_cpu_quota()
+    if quota is not None:
+        n = min(n, max(1, int(quota)))
+    omp = os.environ.get("OMP_NUM_THREADS", "")
+    if omp.isdigit() and int(omp) > 0:
+        n = min(n, int(omp))
+    return max(1, n)
 
 
 def cpu_baseline(w, budget_s: float = 12.0):
@@ -183,7 +239,7 @@ def cpu_baseline(w, budget_s: float = 12.0):
 
     import oracle
 
-    threads = min(16, len(os.sched_getaffinity(0)))
+    threads = host_threads()
     oracle.maxsim_workload(w, docs=np.arange(min(8, w.B)), threads=threads)  # load + warm
     done_docs = 0
     tokens = 0
@@ -205,7 +261,8 @@ def cpu_baseline(w, budget_s: float = 12.0):
         "sample": f"first {done_docs} of {w.B} docs ({tokens} doc tokens"
                   + (f" summed over {w.nq} queries" if w.shared_docs else "")
                   + f") of the same workload, fp64 oracle, {dt:.1f} s wall",
-        "cpu_model": cpu_model(),
+        "cpu_model": cpu_info()["model_name"],
+        "cpu": cpu_info(),
     }
     if w.shared_docs:
         return rec, (np.concatenate(parts, axis=1) if parts else np.zeros((w.nq, 0)))
@@ -267,6 +324,87 @@ def parity_summary(gpu, ref, w):
     return out
 
 
+def percentiles(ms) -> dict:
+    """median, p10, p90, mean, min and max of a list of times."""
+    import numpy as np
+
+    a = np.asarray(ms, np.float64)
+    return {"median": float(np.median(a)), "p10": float(np.percentile(a, 10)),
+            "p90": float(np.percentile(a, 90)), "mean": float(a.mean()), "min": float(a.min()),
+            "max": float(a.max()), "n": int(a.size)}
+
+
+def time_one_shot(w, lir, Q, X, offs, lens, scores, ws, step, dev, args):
+    """Host wall time per call of the one-shot entry point with a synchronise after each
+    call, against the staged step (plan, score, finish on the caller's workspace) timed
+    the same way; reps alternate between the two."""
+    import torch
+
+    if w.shared_docs:
+        return None
+    if w.multi_query:
+        qo, ql, dq = (torch.from_numpy(a).to(dev) for a in (w.q_offsets, w.q_lengths, w.doc_query))
+
+        def call():
+            lir.rerank_pairs(Q, qo, ql, w.Lq, X, offs, lens, dq, scores=scores)
+    elif w.X8 is not None:
+        def call():
+            lir.maxsim_rerank_fp8(Q, X, offs, lens, w.doc_scale, scores=scores)
+    else:
+        def call():
+            lir.rerank(Q, X, offs, lens, scores=scores)
+    reps = 200 if w.doc_bytes < 1e9 else 20
+    for _ in range(5):
+        call()
+        step()
+    torch.cuda.synchronize()
+    one, staged = [], []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        call()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        step()
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        one.append((t1 - t0) * 1e6)
+        staged.append((t2 - t1) * 1e6)
+    a, b = percentiles(one), percentiles(staged)
+    name = ("maxsim_rerank_pairs" if w.multi_query else
+            "maxsim_rerank_fp8" if w.X8 is not None else "maxsim_rerank")
+    return {"entry": name, "reps": reps, "call_us": a, "staged_us": b,
+            "ratio_median": a["median"] / b["median"]}
+
+
+def fp8_quality(gpu, w):
+    """How far FP8 E4M3 storage moves scores and rankings: the GPU's FP8 scores against
+    the fp16 oracle over the same docs before quantisation (all docs)."""
+    import numpy as np
+
+    import oracle
+
+    ref = oracle.maxsim(w.dtype, w.Q, w.X, w.offsets, w.lengths, d=w.d, threads=host_threads())
+    err = np.abs(gpu - ref) / (1.0 + np.abs(ref))
+    n = len(ref)
+    rank_ref = np.empty(n, np.int64)
+    rank_gpu = np.empty(n, np.int64)
+    order_ref = np.lexsort((np.arange(n), -ref))
+    order_gpu = np.lexsort((np.arange(n), -gpu))
+    rank_ref[order_ref] = np.arange(n)
+    rank_gpu[order_gpu] = np.arange(n)
+    out = {"docs": int(n), "reference": "fp16 oracle on the unquantised docs",
+           "max_scaled_err": float(err.max()), "median_scaled_err": float(np.median(err)),
+           "docs_outside_1e-3": int(np.sum(err > 1e-3))}
+    for k in (10, 100):
+        top_ref, top_gpu = order_ref[:k], order_gpu[:k]
+        out[f"top{k}_overlap"] = int(len(set(top_ref.tolist()) & set(top_gpu.tolist())))
+        out[f"top{k}_max_rank_displacement"] = int(np.max(np.abs(rank_gpu[top_ref] - rank_ref[top_ref])))
+    # Spearman rank correlation over all docs
+    out["spearman"] = float(1.0 - 6.0 * np.sum((rank_gpu - rank_ref).astype(np.float64) ** 2)
+                            / (n * (n * n - 1.0)))
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -289,6 +427,12 @@ def main() -> int:
                          "reported as read_ceiling)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="after timing, run one plain 2 GiB device copy (counter calibration)")
+    ap.add_argument("--flush-reps", type=int, default=None,
+                    help="steps timed one by one after a 1 GiB cache-evicting write (default: 200 "
+                         "for workloads under 100 MB of doc rows, 50 under 1 GB, else 20; 0: none)")
+    ap.add_argument("--one-shot", action="store_true",
+                    help="also time the one-shot entry point with a synchronise after every call, "
+                         "against the staged path timed the same way")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -311,7 +455,12 @@ def main() -> int:
 
     log(f"generating workload {args.workload}")
     t0 = time.perf_counter()
-    w = workloads.make(args.workload)
+    if args.workload == "large_fp8" and not args.no_cpu_baseline:
+        # keep the 16-bit docs: the FP8 scores are also compared with the fp16 oracle
+        w = workloads.to_fp8(workloads.large(), keep_x=True)
+        w.name = "large_fp8"
+    else:
+        w = workloads.make(args.workload)
     log(f"generated B={w.B} rows={w.T} doc tokens={w.doc_tokens} in {time.perf_counter() - t0:.1f} s")
     tdt = torch.float16 if w.dtype == "f16" else torch.bfloat16
     Q = torch.from_numpy(w.Q.view(np.int16)).to(dev).view(tdt)
@@ -415,8 +564,34 @@ def main() -> int:
     ms_per_step = total_ms / args.steps
     score_ms = [a.elapsed_time(b) for a, b in evs]
     score_avg_ms = sum(score_ms) / len(score_ms)
+    # Step periods: from one step's score-kernel start to the next one's (the last to the end).
+    step_ms = [evs[i][0].elapsed_time(evs[i + 1][0]) for i in range(args.steps - 1)]
+    step_ms.append(evs[-1][0].elapsed_time(end))
     log(f"timed {args.steps} steps: {ms_per_step:.4f} ms/step, score kernel {score_avg_ms:.4f} ms avg "
         f"(min {min(score_ms):.4f}, max {max(score_ms):.4f})")
+
+    # Flushed: each step right after a 1 GiB write (its own events bracket the step only).
+    flush_reps = args.flush_reps
+    if flush_reps is None:
+        flush_reps = 200 if w.doc_bytes < 100e6 else (50 if w.doc_bytes < 1e9 else 20)
+    flushed = None
+    if flush_reps > 0:
+        evict = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        fl = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(flush_reps)]
+        torch.cuda.synchronize()
+        for i, (s0, a, b, s1) in enumerate(fl):
+            evict.fill_(i & 255)
+            s0.record()
+            step(a, b)
+            s1.record()
+        torch.cuda.synchronize()
+        f_step = [s0.elapsed_time(s1) for s0, _, _, s1 in fl]
+        f_score = [a.elapsed_time(b) for _, a, b, _ in fl]
+        del evict
+        flushed = {"reps": flush_reps, "evict_bytes": 1 << 30,
+                   "step_ms": percentiles(f_step), "score_ms": percentiles(f_score)}
+        log(f"flushed {flush_reps} steps: step median {flushed['step_ms']['median']:.4f} ms, "
+            f"score kernel median {flushed['score_ms']['median']:.4f} ms")
 
     ms_per_step_eager = ms_per_step
     if args.graph:
@@ -449,6 +624,12 @@ def main() -> int:
         torch.cuda.synchronize()
         log("copy probe: one device copy of 2 GiB (reads 2 GiB, writes 2 GiB)")
         del src, dst
+
+    one_shot = None
+    if args.one_shot:
+        one_shot = time_one_shot(w, lir, Q, X, offs, lens, scores, ws, step, dev, args)
+        log(f"one-shot: {one_shot['call_us']['median']:.1f} us per synced call, staged "
+            f"{one_shot['staged_us']['median']:.1f} us (ratio {one_shot['ratio_median']:.2f})")
 
     ceiling = None
     if not args.no_read_probe:
@@ -513,19 +694,27 @@ def main() -> int:
             "avg_launch_ms": launch_ms,
             "launches_per_step": launches,
         },
+        "step_ms": percentiles(step_ms),
+        "score_ms": percentiles(score_ms),
+        "flushed": flushed,
         "cpu_baseline": None,
         "parity": None,
     }
+    if one_shot is not None:
+        rec["one_shot"] = one_shot
     if ceiling is not None:
         ceiling["score_frac_of_ceiling"] = achieved / max(ceiling["lds_dma_GBps"], ceiling["register_GBps"])
         rec["read_ceiling"] = ceiling
     if args.topk:
-        tk_ms = [a.elapsed_time(b) for a, b in tk_events]
+        tk_ms = [a.elapsed_time(b) for a, b in tk_events[: args.steps]]
         rec["topk"] = {"k": args.topk, "avg_ms": sum(tk_ms) / len(tk_ms), "included_in_step": True}
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         rec["cpu_baseline"], ref = cpu_baseline(w)
         rec["parity"] = parity_summary(scores.cpu().numpy(), ref, w)
+        if w.X8 is not None and not w.shared_docs and w.X.shape[0] == w.T:
+            log("fp8 quality: fp16 oracle on the unquantised docs")
+            rec["fp8_quality"] = fp8_quality(scores.cpu().numpy().astype(np.float64), w)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -18,6 +18,17 @@
  *   - Pointers named Q, docs, doc_offsets, doc_lengths, scores and workspace are
  *     DEVICE pointers (any allocator, including PyTorch's caching allocator). The
  *     caller owns every buffer; the library keeps no pointer after the call returns.
+ *   - Scratch of the one-shot entry points (those that take no workspace argument and
+ *     need one: maxsim_rerank[_bf16], _pairs, _multi, _fp8, _topk): the library keeps
+ *     its own workspace per (device, stream), allocated stream-ordered on that stream
+ *     the first time it is needed (and again, larger, when a call needs more), and
+ *     reuses it for every later call on the stream, whose stream order places their
+ *     kernels after the earlier ones. Up to 16 streams per device keep one; a 17th
+ *     stream takes the least recently used stream's, freed stream-ordered after an
+ *     event that follows that stream's last use. A call on a stream that is being
+ *     captured into a HIP graph allocates and frees its workspace inside the capture
+ *     instead (graph memory nodes), so a graph never refers to the cached memory. The
+ *     memory is held until the process ends.
  *   - Q: [Lq, d] row-major, contiguous, same element format as docs, 16-byte aligned.
  *   - docs: rows of `stride` elements (row r starts at element r*stride), unit column
  *     stride, 16-byte aligned. Only columns 0..d-1 of rows inside documents are read;
@@ -74,8 +85,8 @@ extern "C" {
 
 /*
  * MaxSim scores, fp16 Q and docs (IEEE binary16).
- * Allocates its scratch space stream-ordered (hipMallocAsync / hipFreeAsync on
- * `stream`), so concurrent calls on different streams do not interfere.
+ * Uses the stream's one-shot workspace (conventions above), so concurrent calls on
+ * different streams do not interfere; calls from several host threads are safe.
  */
 MAXSIM_API int maxsim_rerank(const void *Q, int32_t Lq, int32_t d,
                   const void *docs, int64_t stride,
@@ -162,7 +173,7 @@ MAXSIM_API int maxsim_rerank_pairs_bf16(const void *Qs, int32_t q_rows, int32_t 
  *            empty query scores 0 against every doc). Read during the call only.
  * scores:    fp32 [nq, B] row-major (device).
  * Other arguments as for maxsim_rerank. Query j's scores equal, bit for bit, those
- * maxsim_rerank gives for query j alone. Allocates its workspace stream-ordered.
+ * maxsim_rerank gives for query j alone. Uses the stream's one-shot workspace.
  */
 MAXSIM_API int maxsim_rerank_multi(const void *Qs, const int32_t *q_lengths, int32_t nq, int32_t d,
                         const void *docs, int64_t stride,
@@ -234,8 +245,8 @@ MAXSIM_API int maxsim_topk(const float *scores, int32_t B, int32_t k, float *top
                 int32_t *top_ids, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
- * maxsim_rerank followed by maxsim_topk in one call: the scores stay in a stream-ordered
- * temporary buffer and only the k best (score, doc index) pairs are written. Arguments
+ * maxsim_rerank followed by maxsim_topk in one call: the scores stay in the stream's
+ * one-shot workspace and only the k best (score, doc index) pairs are written. Arguments
  * as for maxsim_rerank and maxsim_topk.
  */
 MAXSIM_API int maxsim_rerank_topk(const void *Q, int32_t Lq, int32_t d,

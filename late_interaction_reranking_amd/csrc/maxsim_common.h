@@ -69,10 +69,19 @@ struct Layout {
 
 // A doc is split when its bin's upper bound 2^b exceeds the chunk size CT, so every
 // split doc has nt > 2^(b-1) >= CT / 2 tiles: there are fewer than 2 T / CT of them,
-// and, since CT >= T / (kItemsPerWave * W), fewer than 2 * kItemsPerWave * W. Each gets
-// ceil(2^b / CT) < 2 nt / CT + 1 chunks, fewer than 4 * kItemsPerWave * W in all.
-// Split docs come first in the claim order (their bins are the highest), so a split
-// chunk's claim index serves as its slot of per-row maxima.
+// and, since CT >= T / (kItemsPerWave * W), fewer than S = 2 * kItemsPerWave * W; there
+// are also at most B. Each gets ceil(2^b / CT) < 2 nt / CT + 1 chunks, so all of them
+// together have fewer than 2 T / CT + (split docs) <= S + min(B, S) chunks. Split docs
+// come first in the claim order (their bins are the highest), so a split chunk's claim
+// index serves as its slot of per-row maxima. Any W at least the score launch's wave
+// count gives enough slots (the bound grows with W).
+inline uint32_t partial_slots_for(int32_t B, uint32_t waves)
+{
+    const uint64_t s = 2ull * kItemsPerWave * waves;
+    const uint64_t b = B > 0 ? (uint64_t)B : 0ull;
+    return (uint32_t)(s + (b < s ? b : s));
+}
+
 inline Layout make_layout(int lq_pad, int32_t B, uint32_t waves_max)
 {
     Layout L{};
@@ -80,7 +89,7 @@ inline Layout make_layout(int lq_pad, int32_t B, uint32_t waves_max)
     while ((uint64_t)rounds * kPlanBlock * kPlanMaxBlocks < (uint64_t)(B > 0 ? B : 0)) rounds *= 2;
     L.docs_per_plan_block = rounds * kPlanBlock;
     L.plan_blocks = B > 0 ? (uint32_t)(((uint64_t)B + L.docs_per_plan_block - 1) / L.docs_per_plan_block) : 1;
-    L.partial_slots = 4u * kItemsPerWave * waves_max;
+    L.partial_slots = partial_slots_for(B, waves_max);
     L.lq_pad = lq_pad;
     size_t off = 0;
     L.header = off;   off = align256(off + sizeof(Header));

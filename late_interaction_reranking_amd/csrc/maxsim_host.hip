@@ -5,6 +5,8 @@
 // tiles), and FP8 E4M3 docs. The top-k selection lives in maxsim_topk.hip.
 #include "maxsim.h"
 
+#include <string.h>
+
 #include <mutex>
 #include <vector>
 
@@ -728,24 +730,142 @@ int launch_finish(int fmt, int32_t Lq, int32_t d, float *scores, const Layout &L
     return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
 }
 
-// Plan, score and combine with a stream-ordered temporary workspace; qt.max_lq sizes
-// the kernel configuration.
+// ---------------------------------------------------------------- one-shot workspaces
+//
+// The one-shot entry points need scratch space for the schedule and for the per-row
+// maxima of split docs. Taken from hipMallocAsync on every call, that memory is mapped
+// again on every call once the default pool has given it back, which it does at every
+// synchronisation (a 256-doc rerank with a sync per call took 375 us that way, against
+// 56 us with a caller-owned workspace). So the library keeps one workspace per (device,
+// stream) it is called on and reuses it: stream order puts every later call's kernels
+// after the earlier calls' kernels that used it. A workspace that is too small is freed
+// and allocated again, both stream-ordered on its stream.
+//
+// A call on a stream that is being captured into a graph does not use it: its
+// workspace is allocated and freed inside the capture (graph memory nodes), so a graph
+// never refers to memory that an eager call reuses or that the cache frees.
+//
+// kWsSlots streams per device keep a workspace; a new stream takes the least recently
+// used slot. The memory of an evicted slot is freed on the new stream after that stream
+// waits for an event recorded after the slot's last use, so the free is ordered after
+// every kernel that read or wrote it. One lock covers the lookup and the enqueueing of a
+// whole call (host side only: the GPU work of different streams still overlaps).
+constexpr int kWsSlots = 16;
+
+struct WsSlot {
+    hipStream_t stream = nullptr;
+    void *buf = nullptr;
+    size_t bytes = 0;
+    hipEvent_t done = nullptr;  // recorded on `stream` after the last call that used buf
+    uint64_t last = 0;          // use stamp; 0: the slot is free
+};
+
+std::mutex g_ws_mu;
+WsSlot g_ws[kMaxDevices][kWsSlots];
+uint64_t g_ws_clock = 0;
+
+// Whether work enqueued on s now would be captured. An error of the query (for instance
+// on the legacy default stream while another stream captures) counts as capturing: the
+// per-call path needs nothing from the cache.
+bool stream_capturing(hipStream_t s)
+{
+    hipStreamCaptureStatus st = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &st) != hipSuccess) {
+        (void)hipGetLastError();  // do not leave the failed query as the last error
+        return true;
+    }
+    return st != hipStreamCaptureStatusNone;
+}
+
+// Under g_ws_mu: the slot of (current device, s), holding at least `need` bytes.
+int ws_acquire(hipStream_t s, size_t need, WsSlot **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MAXSIM_ERR_HIP;
+    WsSlot *tab = g_ws[dev];
+    WsSlot *slot = nullptr;
+    for (int i = 0; i < kWsSlots && !slot; ++i)
+        if (tab[i].last != 0 && tab[i].stream == s) slot = &tab[i];
+    if (!slot) {
+        slot = &tab[0];  // free slots (last == 0) first, then the least recently used
+        for (int i = 1; i < kWsSlots; ++i)
+            if (tab[i].last < slot->last) slot = &tab[i];
+        if (slot->buf) {
+            if (hipStreamWaitEvent(s, slot->done, 0) != hipSuccess) return MAXSIM_ERR_HIP;
+            if (hipFreeAsync(slot->buf, s) != hipSuccess) return MAXSIM_ERR_HIP;
+            slot->buf = nullptr;
+            slot->bytes = 0;
+        }
+        if (!slot->done && hipEventCreateWithFlags(&slot->done, hipEventDisableTiming) != hipSuccess) {
+            slot->done = nullptr;
+            return MAXSIM_ERR_HIP;
+        }
+        slot->stream = s;
+    }
+    slot->last = ++g_ws_clock;
+    if (slot->bytes < need) {
+        if (slot->buf) {
+            if (hipFreeAsync(slot->buf, s) != hipSuccess) return MAXSIM_ERR_HIP;
+            slot->buf = nullptr;
+            slot->bytes = 0;
+        }
+        // A quarter more than asked, in whole MiB, so that a slowly growing batch does
+        // not reallocate on every call.
+        const size_t want = ((need + need / 4) + ((size_t)1 << 20) - 1) & ~(((size_t)1 << 20) - 1);
+        void *p = nullptr;
+        if (hipMallocAsync(&p, want, s) != hipSuccess) return MAXSIM_ERR_HIP;
+        slot->buf = p;
+        slot->bytes = want;
+    }
+    *out = slot;
+    return MAXSIM_OK;
+}
+
+// Runs enqueue(w) with w a 256-byte aligned workspace of at least `need` bytes on s.
+template <class F>
+int with_workspace(hipStream_t s, size_t need, F &&enqueue)
+{
+    if (need == 0) need = 256;
+    if (stream_capturing(s)) {
+        void *ws = nullptr;
+        if (hipMallocAsync(&ws, need, s) != hipSuccess) return MAXSIM_ERR_HIP;
+        int rc = enqueue(static_cast<char *>(ws));
+        if (hipFreeAsync(ws, s) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
+        return rc;
+    }
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    WsSlot *slot = nullptr;
+    int rc = ws_acquire(s, need, &slot);
+    if (rc != MAXSIM_OK) return rc;
+    rc = enqueue(static_cast<char *>(slot->buf));
+    if (hipEventRecord(slot->done, s) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
+    return rc;
+}
+
+// Plan, score and combine into the workspace w (layout L); qt.max_lq sizes the kernel
+// configuration.
+int enqueue_all(int fmt, const void *Q, const QueryTable &qt, int32_t d, const void *docs, int64_t stride,
+                const int32_t *offsets, const int32_t *lengths, int32_t B, float *scores, float doc_scale,
+                const Layout &L, char *w, hipStream_t stream)
+{
+    const QueryTiles tiles = single_tiles(qt.max_lq);  // (a pairs plan ignores them)
+    int rc = launch_plan(offsets, lengths, B, L, qt, w, stream);
+    if (rc == MAXSIM_OK)
+        rc = launch_score(fmt, Q, qt.max_lq, d, docs, stride, scores, L, w, tiles, doc_scale, stream);
+    if (rc == MAXSIM_OK) rc = launch_finish(fmt, qt.max_lq, d, scores, L, w, tiles, doc_scale, stream);
+    return rc;
+}
+
+// Plan, score and combine with the stream's one-shot workspace.
 int run_all(int fmt, const void *Q, const QueryTable &qt, int32_t d, const void *docs,
             int64_t stride, const int32_t *offsets, const int32_t *lengths, int32_t B, float *scores,
             float doc_scale, hipStream_t stream)
 {
     Layout L;
     if (workspace_layout(qt.max_lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
-    void *ws = nullptr;
-    if (hipMallocAsync(&ws, L.total, stream) != hipSuccess) return MAXSIM_ERR_HIP;
-    char *w = static_cast<char *>(ws);
-    const QueryTiles tiles = single_tiles(qt.max_lq);  // (a pairs plan ignores them)
-    int rc = launch_plan(offsets, lengths, B, L, qt, w, stream);
-    if (rc == MAXSIM_OK)
-        rc = launch_score(fmt, Q, qt.max_lq, d, docs, stride, scores, L, w, tiles, doc_scale, stream);
-    if (rc == MAXSIM_OK) rc = launch_finish(fmt, qt.max_lq, d, scores, L, w, tiles, doc_scale, stream);
-    if (hipFreeAsync(ws, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
-    return rc;
+    return with_workspace(stream, L.total, [&](char *w) {
+        return enqueue_all(fmt, Q, qt, d, docs, stride, offsets, lengths, B, scores, doc_scale, L, w, stream);
+    });
 }
 
 int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
@@ -759,11 +879,23 @@ int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, in
     return run_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, stream);
 }
 
+// A usable scale of FP8 docs: positive and at most 3.4e38 (so finite), never NaN. The
+// test runs on the bit pattern: a positive float's bits grow with its value, and zero,
+// negative values, infinity and NaN all fall outside (0, bits(3.4e38)]. No compare of
+// floats is involved, so no assumption a compiler may make about NaN can change it.
+bool valid_scale(float s)
+{
+    uint32_t bits;
+    memcpy(&bits, &s, sizeof bits);
+    constexpr uint32_t kMaxScaleBits = 0x7F7FC99Eu;  // 3.4e38f
+    return bits - 1u < kMaxScaleBits;
+}
+
 // Extra checks for docs stored as FP8 E4M3 bytes: whole 16-byte chunks per row and a
 // finite positive scale.
 int check_fp8(int32_t d, int64_t stride, float doc_scale)
 {
-    if (!(doc_scale > 0.0f) || doc_scale > 3.4e38f) return MAXSIM_ERR_INVALID_ARG;
+    if (!valid_scale(doc_scale)) return MAXSIM_ERR_INVALID_ARG;
     if (d % 16 != 0 || stride % 16 != 0) return MAXSIM_ERR_UNSUPPORTED;
     return MAXSIM_OK;
 }
@@ -818,7 +950,7 @@ int rerank_short(int fmt, const void *Q, int32_t Lq, int32_t d, const void *docs
     return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
 }
 
-// Scores into a stream-ordered temporary buffer, then the device top-k of them.
+// Scores into the stream's one-shot workspace, then the device top-k of them.
 int rerank_topk(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
                 const int32_t *offsets, const int32_t *lengths, int32_t B, int32_t k, float *top_scores,
                 int32_t *top_ids, void *stream_ptr)
@@ -832,21 +964,26 @@ int rerank_topk(int dtype, const void *Q, int32_t Lq, int32_t d, const void *doc
     if (st != MAXSIM_OK) return st;
     if (k == 0) return MAXSIM_OK;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    // Workspace: rerank layout (when there is one), then the scores, then the top-k's.
+    Layout L{};
+    const bool ranked = B > 0 && Lq > 0;
+    if (ranked && workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    const size_t score_at = ranked ? L.total : 0;
     const size_t score_bytes = ((size_t)(B > 0 ? B : 1) * 4 + 255) & ~size_t(255);
-    void *buf = nullptr;
-    if (hipMallocAsync(&buf, score_bytes + topk_workspace_bytes(B, k), stream) != hipSuccess) return MAXSIM_ERR_HIP;
-    float *scores = static_cast<float *>(buf);
-    int rc = MAXSIM_OK;
-    if (B > 0) {
-        if (Lq == 0)
-            rc = launch_fill(scores, B, 0.0f, stream);
-        else
-            rc = run_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, stream);
-    }
-    if (rc == MAXSIM_OK)
-        rc = launch_topk(scores, B, k, top_scores, top_ids, static_cast<char *>(buf) + score_bytes, stream);
-    if (hipFreeAsync(buf, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
-    return rc;
+    const size_t need = score_at + score_bytes + topk_workspace_bytes(B, k);
+    return with_workspace(stream, need, [&](char *w) {
+        float *scores = reinterpret_cast<float *>(w + score_at);
+        int rc = MAXSIM_OK;
+        if (B > 0) {
+            if (!ranked)
+                rc = launch_fill(scores, B, 0.0f, stream);
+            else
+                rc = enqueue_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, L,
+                                 w, stream);
+        }
+        if (rc == MAXSIM_OK) rc = launch_topk(scores, B, k, top_scores, top_ids, w + score_at + score_bytes, stream);
+        return rc;
+    });
 }
 
 int rerank_fp8(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
@@ -968,36 +1105,34 @@ int rerank_multi(int fmt, const void *Qs, const int32_t *q_lengths, int32_t nq, 
     DeviceFacts f;
     if (current_facts(&f) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     const Layout L = make_layout(max_pad, B, (uint32_t)(f.cus * f.waves_per_cu));
-    void *ws = nullptr;
-    if (hipMallocAsync(&ws, L.total, stream) != hipSuccess) return MAXSIM_ERR_HIP;
-    char *w = static_cast<char *>(ws);
-    rc = launch_plan(offsets, lengths, B, L, single_query(0), w, stream);
-    const char *qbytes = static_cast<const char *>(Qs);
-    for (size_t p = 0; p < passes.size() && rc == MAXSIM_OK; ++p) {
-        const Pass &ps = passes[p];
-        QueryTiles qt{};
-        qt.score_stride = B;
-        for (int T = 0; T < kMaxQTiles; ++T) qt.set(T, 0, 0, -1);
-        int T = 0;
-        int64_t rel = 0;  // row of query j relative to the pass
-        for (int32_t j = ps.j0; j < ps.j1; ++j) {
-            const int Lj = q_lengths[j];
-            const int t = (Lj + kTileRows - 1) / kTileRows;
-            for (int k = 0; k < t; ++k, ++T) {
-                const int left = Lj - k * kTileRows;
-                qt.set(T, (int)(rel + k * kTileRows), left > kTileRows ? kTileRows : left,
-                       k == t - 1 ? j - ps.j0 : -1);
+    return with_workspace(stream, L.total, [&](char *w) {
+        int rc = launch_plan(offsets, lengths, B, L, single_query(0), w, stream);
+        const char *qbytes = static_cast<const char *>(Qs);
+        for (size_t p = 0; p < passes.size() && rc == MAXSIM_OK; ++p) {
+            const Pass &ps = passes[p];
+            QueryTiles qt{};
+            qt.score_stride = B;
+            for (int T = 0; T < kMaxQTiles; ++T) qt.set(T, 0, 0, -1);
+            int T = 0;
+            int64_t rel = 0;  // row of query j relative to the pass
+            for (int32_t j = ps.j0; j < ps.j1; ++j) {
+                const int Lj = q_lengths[j];
+                const int t = (Lj + kTileRows - 1) / kTileRows;
+                for (int k = 0; k < t; ++k, ++T) {
+                    const int left = Lj - k * kTileRows;
+                    qt.set(T, (int)(rel + k * kTileRows), left > kTileRows ? kTileRows : left,
+                           k == t - 1 ? j - ps.j0 : -1);
+                }
+                rel += Lj;
             }
-            rel += Lj;
+            const void *Qp = qbytes + (size_t)ps.row0 * (size_t)d * 2;
+            float *sp = scores + (size_t)ps.j0 * (size_t)B;
+            const int rows = ps.tiles * kTileRows;
+            rc = launch_score(fmt, Qp, rows, d, docs, stride, sp, L, w, qt, doc_scale, stream);
+            if (rc == MAXSIM_OK) rc = launch_finish(fmt, rows, d, sp, L, w, qt, doc_scale, stream);
         }
-        const void *Qp = qbytes + (size_t)ps.row0 * (size_t)d * 2;
-        float *sp = scores + (size_t)ps.j0 * (size_t)B;
-        const int rows = ps.tiles * kTileRows;
-        rc = launch_score(fmt, Qp, rows, d, docs, stride, sp, L, w, qt, doc_scale, stream);
-        if (rc == MAXSIM_OK) rc = launch_finish(fmt, rows, d, sp, L, w, qt, doc_scale, stream);
-    }
-    if (hipFreeAsync(ws, stream) != hipSuccess && rc == MAXSIM_OK) rc = MAXSIM_ERR_HIP;
-    return rc;
+        return rc;
+    });
 }
 
 // Bodies of the staged score and finish entries; fmt is already checked.
@@ -1243,7 +1378,7 @@ int maxsim_finish_fp8(int dtype, int32_t Lq, int32_t d, int32_t B, float doc_sca
                       void *workspace, size_t workspace_bytes, void *stream)
 {
     if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
-    if (!(doc_scale > 0.0f) || doc_scale > 3.4e38f) return MAXSIM_ERR_INVALID_ARG;
+    if (!valid_scale(doc_scale)) return MAXSIM_ERR_INVALID_ARG;
     if (d % 16 != 0) return MAXSIM_ERR_UNSUPPORTED;
     return staged_finish(dtype | kFmtFp8Docs, Lq, d, B, scores, workspace, workspace_bytes, doc_scale,
                          static_cast<hipStream_t>(stream));

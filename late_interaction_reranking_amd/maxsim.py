@@ -216,12 +216,22 @@ def _marshal(Q, docs, doc_offsets, doc_lengths, dtype):
     return Lq, d, stride, int(doc_offsets.shape[0])
 
 
+def _scores_out(scores, shape, dev) -> torch.Tensor:
+    """A new fp32 score tensor of `shape` on `dev`, or the caller's after checking that it
+    is one: contiguous fp32 of that shape on the same GPU as the docs (the kernels store
+    through its pointer, so a tensor on the host or on another GPU must never reach them)."""
+    if scores is None:
+        return torch.empty(shape, dtype=torch.float32, device=dev)
+    if scores.dtype != torch.float32 or tuple(scores.shape) != tuple(shape) or not scores.is_contiguous():
+        raise ValueError(f"scores must be a contiguous float32 {list(shape)} tensor")
+    if scores.device != dev:
+        raise ValueError(f"scores must live on {dev}, with docs (got {scores.device})")
+    return scores
+
+
 def _rerank(fn_name, dtype, Q, docs, doc_offsets, doc_lengths, scores=None):
     Lq, d, stride, B = _marshal(Q, docs, doc_offsets, doc_lengths, dtype)
-    if scores is None:
-        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
-    elif scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
-        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    scores = _scores_out(scores, (B,), docs.device)
     with torch.cuda.device(docs.device):
         st = getattr(load(), fn_name)(
             Q.data_ptr(), Lq, d, docs.data_ptr(), stride, doc_offsets.data_ptr(),
@@ -253,10 +263,7 @@ def maxsim_rerank_short(Q, docs, doc_offsets, doc_lengths, scores=None) -> torch
     docs); fp16 or bf16 by Q's dtype. Bitwise equal to maxsim_rerank."""
     dtype = torch.bfloat16 if Q.dtype == torch.bfloat16 else torch.float16
     Lq, d, stride, B = _marshal(Q, docs, doc_offsets, doc_lengths, dtype)
-    if scores is None:
-        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
-    elif scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
-        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    scores = _scores_out(scores, (B,), docs.device)
     code = MAXSIM_BF16 if dtype == torch.bfloat16 else MAXSIM_F16
     with torch.cuda.device(docs.device):
         st = load().maxsim_rerank_short(
@@ -280,9 +287,13 @@ def maxsim_workspace_size(Lq: int, d: int, B: int, device=None) -> int:
     return int(n.value)
 
 
-def _ws(workspace: torch.Tensor) -> tuple[int, int]:
+def _ws(workspace: torch.Tensor, dev=None) -> tuple[int, int]:
+    """Pointer and size of a caller workspace: a contiguous uint8 tensor on the GPU, on
+    `dev` (the device of the tensors the call reads or writes) when given."""
     if workspace.dtype != torch.uint8 or not workspace.is_contiguous() or workspace.device.type != "cuda":
         raise ValueError("workspace must be a contiguous uint8 GPU tensor")
+    if dev is not None and workspace.device != dev:
+        raise ValueError(f"workspace must live on {dev}, with the other tensors (got {workspace.device})")
     return workspace.data_ptr(), int(workspace.numel())
 
 
@@ -290,6 +301,8 @@ def maxsim_plan(doc_offsets, doc_lengths, Lq: int, d: int, workspace: torch.Tens
     """Enqueue the length-binned schedule into `workspace` on the current stream."""
     if doc_offsets.dtype != torch.int32 or doc_lengths.dtype != torch.int32:
         raise TypeError("doc_offsets and doc_lengths must be int32")
+    if doc_offsets.device != workspace.device or doc_lengths.device != workspace.device:
+        raise ValueError("doc_offsets and doc_lengths must live on the workspace's GPU")
     ptr, nbytes = _ws(workspace)
     with torch.cuda.device(workspace.device):
         st = load().maxsim_plan(doc_offsets.data_ptr(), doc_lengths.data_ptr(), int(doc_offsets.shape[0]),
@@ -305,9 +318,8 @@ def maxsim_score(Q, docs, doc_offsets, doc_lengths, workspace: torch.Tensor, sco
     dtype = torch.bfloat16 if Q.dtype == torch.bfloat16 else torch.float16
     q_rows, d, stride, B = _marshal(Q, docs, doc_offsets, doc_lengths, dtype)
     Lq = q_rows if Lq is None else int(Lq)
-    if scores is None:
-        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
-    ptr, nbytes = _ws(workspace)
+    scores = _scores_out(scores, (B,), docs.device)
+    ptr, nbytes = _ws(workspace, docs.device)
     code = MAXSIM_BF16 if dtype == torch.bfloat16 else MAXSIM_F16
     with torch.cuda.device(docs.device):
         st = load().maxsim_score(code, Q.data_ptr(), Lq, d, docs.data_ptr(), stride,
@@ -323,10 +335,11 @@ def maxsim_finish(Q, B: int, workspace: torch.Tensor, scores: torch.Tensor,
     work items. Q only supplies d, the element format and, unless given, Lq."""
     if Q.dim() != 2:
         raise ValueError("Q must be 2-D")
-    if scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
-        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    if scores is None or scores.device.type != "cuda":
+        raise ValueError("scores must be a GPU tensor")
+    scores = _scores_out(scores, (B,), scores.device)
     code = MAXSIM_BF16 if Q.dtype == torch.bfloat16 else MAXSIM_F16
-    ptr, nbytes = _ws(workspace)
+    ptr, nbytes = _ws(workspace, scores.device)
     with torch.cuda.device(workspace.device):
         st = load().maxsim_finish(code, int(Q.shape[0]) if Lq is None else int(Lq), int(Q.shape[1]),
                                   int(B), scores.data_ptr(),
@@ -352,10 +365,7 @@ def _rerank_pairs(fn_name, dtype, Qs, q_offsets, q_lengths, max_lq, docs, doc_of
         raise ValueError("q_offsets and q_lengths must have one entry per query")
     if doc_query.shape[0] != B:
         raise ValueError("doc_query must have one entry per doc")
-    if scores is None:
-        scores = torch.empty(B, dtype=torch.float32, device=dev)
-    elif scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
-        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    scores = _scores_out(scores, (B,), dev)
     with torch.cuda.device(dev):
         st = getattr(load(), fn_name)(
             Qs.data_ptr(), int(Qs.shape[0]), d, q_offsets.data_ptr(), q_lengths.data_ptr(),
@@ -414,10 +424,7 @@ def _rerank_multi(fn_name, dtype, Qs, q_lengths, docs, doc_offsets, doc_lengths,
     if sum(ql) != Qs.shape[0]:
         raise ValueError("Qs must hold exactly the rows of the queries, back to back")
     host = (ctypes.c_int32 * max(nq, 1))(*ql)
-    if scores is None:
-        scores = torch.empty((nq, B), dtype=torch.float32, device=docs.device)
-    elif scores.dtype != torch.float32 or tuple(scores.shape) != (nq, B) or not scores.is_contiguous():
-        raise ValueError("scores must be a contiguous float32 [nq, B] tensor")
+    scores = _scores_out(scores, (nq, B), docs.device)
     with torch.cuda.device(docs.device):
         st = getattr(load(), fn_name)(
             Qs.data_ptr(), ctypes.cast(host, ctypes.c_void_p), nq, d, docs.data_ptr(), stride,
@@ -477,10 +484,7 @@ def maxsim_rerank_fp8(Q, docs, doc_offsets, doc_lengths, doc_scale: float, score
     """fp32 [B] MaxSim scores with docs stored as FP8 E4M3 bytes (element = doc_scale *
     e4m3) and an fp16 or bf16 query; d and the row stride (bytes) multiples of 16."""
     Lq, d, stride, B = _check_fp8_args(Q, docs, doc_offsets, doc_lengths)
-    if scores is None:
-        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
-    elif scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
-        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    scores = _scores_out(scores, (B,), docs.device)
     name = "maxsim_rerank_fp8_bf16" if Q.dtype == torch.bfloat16 else "maxsim_rerank_fp8"
     with torch.cuda.device(docs.device):
         st = getattr(load(), name)(Q.data_ptr(), Lq, d, docs.data_ptr(), stride, doc_offsets.data_ptr(),
@@ -494,10 +498,7 @@ def maxsim_rerank_short_fp8(Q, docs, doc_offsets, doc_lengths, doc_scale: float,
     """maxsim_rerank_fp8's scores in one launch, one workgroup per doc (for batches of
     short docs); bitwise equal to maxsim_rerank_fp8 with the same query dtype."""
     Lq, d, stride, B = _check_fp8_args(Q, docs, doc_offsets, doc_lengths)
-    if scores is None:
-        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
-    elif scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
-        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    scores = _scores_out(scores, (B,), docs.device)
     code = MAXSIM_BF16 if Q.dtype == torch.bfloat16 else MAXSIM_F16
     with torch.cuda.device(docs.device):
         st = load().maxsim_rerank_short_fp8(code, Q.data_ptr(), Lq, d, docs.data_ptr(), stride,
@@ -511,9 +512,8 @@ def maxsim_score_fp8(Q, docs, doc_offsets, doc_lengths, doc_scale: float, worksp
                      scores=None) -> torch.Tensor:
     """Staged score kernel for FP8 E4M3 docs over a schedule maxsim_plan wrote."""
     Lq, d, stride, B = _check_fp8_args(Q, docs, doc_offsets, doc_lengths)
-    if scores is None:
-        scores = torch.empty(B, dtype=torch.float32, device=docs.device)
-    ptr, nbytes = _ws(workspace)
+    scores = _scores_out(scores, (B,), docs.device)
+    ptr, nbytes = _ws(workspace, docs.device)
     code = MAXSIM_BF16 if Q.dtype == torch.bfloat16 else MAXSIM_F16
     with torch.cuda.device(docs.device):
         st = load().maxsim_score_fp8(code, Q.data_ptr(), Lq, d, docs.data_ptr(), stride, doc_offsets.data_ptr(),
@@ -527,10 +527,11 @@ def maxsim_finish_fp8(Q, B: int, doc_scale: float, workspace: torch.Tensor, scor
     """Staged combine step for FP8 E4M3 docs (Q supplies Lq, d and its format)."""
     if Q.dim() != 2:
         raise ValueError("Q must be 2-D")
-    if scores.dtype != torch.float32 or scores.shape != (B,) or not scores.is_contiguous():
-        raise ValueError("scores must be a contiguous float32 [B] tensor")
+    if scores is None or scores.device.type != "cuda":
+        raise ValueError("scores must be a GPU tensor")
+    scores = _scores_out(scores, (B,), scores.device)
     code = MAXSIM_BF16 if Q.dtype == torch.bfloat16 else MAXSIM_F16
-    ptr, nbytes = _ws(workspace)
+    ptr, nbytes = _ws(workspace, scores.device)
     with torch.cuda.device(workspace.device):
         st = load().maxsim_finish_fp8(code, int(Q.shape[0]), int(Q.shape[1]), int(B), float(doc_scale),
                                       scores.data_ptr(), ptr, nbytes, _stream(workspace))
@@ -553,7 +554,7 @@ def maxsim_topk(scores: torch.Tensor, k: int, workspace: torch.Tensor | None = N
     _check(load().maxsim_topk_workspace_size(B, k, ctypes.byref(n)), "maxsim_topk_workspace_size")
     if workspace is None:
         workspace = torch.empty(int(n.value), dtype=torch.uint8, device=dev)
-    ptr, nbytes = _ws(workspace)
+    ptr, nbytes = _ws(workspace, dev)
     top_scores = torch.empty(k, dtype=torch.float32, device=dev)
     top_ids = torch.empty(k, dtype=torch.int32, device=dev)
     with torch.cuda.device(dev):
@@ -592,8 +593,7 @@ def maxsim_rerank_pairs_fp8(Qs, q_offsets, q_lengths, max_lq: int, docs, doc_off
         _int32_vec(t, name, dev)
     if q_offsets.shape != q_lengths.shape or doc_query.shape[0] != B:
         raise ValueError("q_offsets / q_lengths: one entry per query; doc_query: one per doc")
-    if scores is None:
-        scores = torch.empty(B, dtype=torch.float32, device=dev)
+    scores = _scores_out(scores, (B,), dev)
     code = MAXSIM_BF16 if Qs.dtype == torch.bfloat16 else MAXSIM_F16
     with torch.cuda.device(dev):
         st = load().maxsim_rerank_pairs_fp8(
@@ -614,8 +614,7 @@ def maxsim_rerank_multi_fp8(Qs, q_lengths, docs, doc_offsets, doc_lengths, doc_s
     if sum(ql) != Qs.shape[0]:
         raise ValueError("Qs must hold exactly the rows of the queries, back to back")
     host = (ctypes.c_int32 * max(nq, 1))(*ql)
-    if scores is None:
-        scores = torch.empty((nq, B), dtype=torch.float32, device=docs.device)
+    scores = _scores_out(scores, (nq, B), docs.device)
     code = MAXSIM_BF16 if Qs.dtype == torch.bfloat16 else MAXSIM_F16
     with torch.cuda.device(docs.device):
         st = load().maxsim_rerank_multi_fp8(code, Qs.data_ptr(), ctypes.cast(host, ctypes.c_void_p), nq, d,

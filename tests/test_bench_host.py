@@ -66,3 +66,43 @@ def test_score_launches_mirror_the_pass_rule():
     m = workloads.custom_multi([200, 0, 5], 128, np.full(3, 5), seed=1)
     assert bench.score_launches(m) == 2          # a 13-tile query alone, then the 1-tile one
     assert bench.score_launches(workloads.custom(8, 32, [3], seed=1)) == 1
+
+
+def test_percentiles():
+    p = bench.percentiles(list(range(1, 102)))
+    assert p["median"] == 51 and p["p10"] == 11 and p["p90"] == 91 and p["n"] == 101
+    assert p["min"] == 1 and p["max"] == 101
+
+
+def test_host_threads_respect_affinity_and_share(monkeypatch):
+    n_aff = len(os.sched_getaffinity(0))
+    monkeypatch.delenv("OMP_NUM_THREADS", raising=False)
+    monkeypatch.setattr(bench, "cgroup_cpu_quota", lambda: None)
+    assert bench.host_threads() == n_aff
+    monkeypatch.setenv("OMP_NUM_THREADS", "1")
+    assert bench.host_threads() == 1
+    monkeypatch.delenv("OMP_NUM_THREADS")
+    monkeypatch.setattr(bench, "cgroup_cpu_quota", lambda: 2.5)
+    assert bench.host_threads() == min(n_aff, 2)
+    info = bench.cpu_info()
+    assert info["affinity_cpus"] == n_aff and isinstance(info["model_name"], str)
+
+
+def test_fp8_quality_against_the_fp16_oracle():
+    """The quality report on a small workload, with the FP8 oracle's scores standing in
+    for the GPU's: quantised scores stay near the fp16 ones, the report's rank and
+    overlap figures are consistent, and the unquantised scores themselves score perfectly."""
+    import oracle
+
+    w = workloads.custom(32, 128, np.random.default_rng(3).integers(16, 200, size=400), seed=3)
+    workloads.to_fp8(w, keep_x=True)
+    ref16 = oracle.maxsim(w.dtype, w.Q, w.X, w.offsets, w.lengths, d=w.d)
+    q8 = oracle.maxsim_fp8(w.dtype, w.Q, w.X8, w.offsets, w.lengths, w.doc_scale, d=w.d)
+    out = bench.fp8_quality(q8, w)
+    assert out["docs"] == 400
+    assert 0 < out["max_scaled_err"] < 0.05
+    assert 0 <= out["top10_overlap"] <= 10 and out["top100_overlap"] <= 100
+    assert out["spearman"] > 0.9
+    same = bench.fp8_quality(ref16, w)
+    assert same["max_scaled_err"] == 0.0 and same["top10_overlap"] == 10
+    assert same["top10_max_rank_displacement"] == 0 and abs(same["spearman"] - 1.0) < 1e-12

@@ -18,6 +18,12 @@ def bin_of(nt):
     return 0 if nt <= 1 else int(nt - 1).bit_length()
 
 
+def slots(B, waves):
+    """Partial-maxima slots the library reserves (maxsim_common.h, partial_slots_for)."""
+    s = 2 * ITEMS_PER_WAVE * waves
+    return s + min(B, s)
+
+
 def schedule(lengths, waves, nqt=1):
     nt = [(int(n) + 15) // 16 for n in lengths]
     T = sum(nt)
@@ -61,9 +67,40 @@ def test_schedule_covers_and_fits(seed, waves, nqt):
         covered[i].append((a, b))
         if K > 1:
             assert desc < 2 * ITEMS_PER_WAVE * waves
-            assert claim < 4 * ITEMS_PER_WAVE * waves
+            assert desc < len(lengths)
+            assert claim < slots(len(lengths), waves)
     for i, rngs in enumerate(covered):
         rngs.sort()
         assert rngs[0][0] == 0 and rngs[-1][1] == nt[i]
         for (a0, b0), (a1, b1) in zip(rngs, rngs[1:]):
             assert b0 == a1
+
+
+def split_claims(lengths, waves, nqt=1):
+    """Number of work items of split docs (slots of per-row maxima the launch writes)."""
+    _, items = schedule(lengths, waves, nqt)
+    return sum(1 for it in items if it[4] > 1)
+
+
+@pytest.mark.parametrize("waves", [4, 12, 64, 768, 3072])
+@pytest.mark.parametrize("nqt", [1, 2, 8])
+def test_slot_bound_adversarial(waves, nqt):
+    """Docs of 2^(b-1) + 1 tiles get the most chunks per tile (ceil(2^b / CT) chunks for
+    just over half of 2^b tiles); mixed with filler docs that raise or lower T, and with
+    B around the 8 W split-doc bound, these come closest to the reserved slot count."""
+    rng = np.random.default_rng(waves * 10 + nqt)
+    worst = 0.0
+    for trial in range(60):
+        b = int(rng.integers(1, 14))
+        n_big = int(rng.integers(1, 3 * 8 * waves + 2))
+        big = np.full(n_big, ((1 << (b - 1)) + 1) * 16 - int(rng.integers(0, 16)))
+        n_small = int(rng.integers(0, 2 * waves + 1))
+        small = rng.integers(0, 40, size=n_small)
+        lengths = np.concatenate([big, small])
+        if len(lengths) > 40000:
+            lengths = lengths[:40000]
+        used = split_claims(lengths, waves, nqt)
+        cap = slots(len(lengths), waves)
+        assert used <= cap, (b, len(lengths), used, cap)
+        worst = max(worst, used / cap)
+    assert worst > 0.0

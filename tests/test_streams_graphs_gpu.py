@@ -137,3 +137,80 @@ def test_graph_pairs_multi_fp8():
                 lir.maxsim_rerank_fp8(Qf, Xf, offf, lenf, wf.doc_scale))
 
     _replays(g, change, eager, (op, om, of))
+
+
+def _staged(Q, X, offs, lens):
+    """Scores from the staged path on a fresh caller workspace (no library cache)."""
+    B = int(offs.shape[0])
+    ws = torch.empty(lir.maxsim_workspace_size(Q.shape[0], Q.shape[1], B), dtype=torch.uint8, device=DEV)
+    lir.maxsim_plan(offs, lens, Q.shape[0], Q.shape[1], ws)
+    out = lir.maxsim_score(Q, X, offs, lens, ws)
+    lir.maxsim_finish(Q, B, ws, out)
+    return out
+
+
+def test_one_shot_workspace_cache_reuse_growth_eviction():
+    """The one-shot entry points keep a workspace per stream: batches that grow and
+    shrink on one stream with no synchronisation between calls, then more streams than
+    the library keeps workspaces for (so workspaces are evicted and freed while other
+    streams run), every result bitwise the staged path's on its own workspace."""
+    _say("[streams] one-shot workspace cache")
+    rng = np.random.default_rng(11)
+    shapes = [(300, 500), (3000, 2000), (50, 40), (1000, 9000), (200, 100), (4000, 300)]
+    ws = [workloads.custom(32, 128, rng.integers(0, n, size=b), seed=20 + i, order="shuffled")
+          for i, (n, b) in enumerate(shapes)]
+    ups = [upload(w) for w in ws]
+    refs = [_staged(*u) for u in ups]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    outs = []
+    with torch.cuda.stream(s):
+        for _ in range(3):
+            for k, u in enumerate(ups):
+                outs.append((k, lir.rerank(*u)))
+    torch.cuda.synchronize()
+    for k, o in outs:
+        assert torch.equal(o, refs[k]), f"same stream, batch {k}"
+    streams = [torch.cuda.Stream() for _ in range(21)]
+    outs = []
+    for rep in range(3):
+        for j, st in enumerate(streams):
+            st.wait_stream(torch.cuda.current_stream())
+            k = (j + rep) % len(ups)
+            with torch.cuda.stream(st):
+                outs.append((k, lir.rerank(*ups[k])))
+                outs.append((-1 - k, lir.maxsim_rerank_topk(*ups[k], 20)))
+    torch.cuda.synchronize()
+    for k, o in outs:
+        if k >= 0:
+            assert torch.equal(o, refs[k]), f"many streams, batch {k}"
+        else:
+            ref_s, ref_i = lir.maxsim_topk(refs[-1 - k], 20)
+            assert torch.equal(o[0], ref_s) and torch.equal(o[1], ref_i), f"top-k, batch {-1 - k}"
+
+
+def test_eager_calls_after_a_captured_one_shot_on_the_same_stream():
+    """A graph captured on a stream that already holds a cached workspace refers only to
+    its own graph memory: eager calls on that stream between replays, with other inputs,
+    leave the replays' results intact, and the replays leave theirs."""
+    _say("[graph] captured one-shot next to eager calls on the same stream")
+    rng = np.random.default_rng(12)
+    wa = workloads.custom(32, 128, rng.integers(0, 700, size=1500), seed=30, order="shuffled")
+    wb = workloads.custom(32, 128, rng.integers(0, 2500, size=600), seed=31, order="shuffled")
+    A, Bw = upload(wa), upload(wb)
+    ref_a, ref_b = _staged(*A), _staged(*Bw)
+    out = torch.empty(wa.B, dtype=torch.float32, device=DEV)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = _capture(lambda: lir.rerank(*A, scores=out), s)
+    for _ in range(3):
+        out.zero_()
+        torch.cuda.synchronize()
+        with torch.cuda.stream(s):
+            eb = lir.rerank(*Bw)
+            g.replay()
+            eb2 = lir.rerank(*Bw)
+        torch.cuda.synchronize()
+        assert torch.equal(out, ref_a)
+        assert torch.equal(eb, ref_b) and torch.equal(eb2, ref_b)
