@@ -78,6 +78,7 @@ extern "C" {
 #define MAXSIM_ERR_UNSUPPORTED 2 /* outside the supported envelope above                */
 #define MAXSIM_ERR_HIP 3         /* a HIP call failed (no device, allocation, launch)   */
 #define MAXSIM_ERR_WORKSPACE 4   /* caller workspace null, misaligned or too small      */
+#define MAXSIM_ERR_SCRATCH 5     /* batch needs more than maxsim_rerank_noalloc's scratch */
 
 /* Element formats of Q and docs for the staged entry points. */
 #define MAXSIM_F16 0
@@ -120,6 +121,29 @@ MAXSIM_API int maxsim_rerank_short(int dtype, const void *Q, int32_t Lq, int32_t
                         const void *docs, int64_t stride,
                         const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
                         float *scores, void *stream);
+
+/*
+ * maxsim_rerank for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same plan, score
+ * and combine kernels as maxsim_rerank, so the same scores bit for bit, with a fixed
+ * scratch array in device memory as their workspace instead of an allocation: 64 MiB
+ * per GPU, reserved when the library is first used on that GPU and held until the
+ * process ends. The call allocates nothing (no hipMalloc, hipMallocAsync or hipFree).
+ * dtype: MAXSIM_F16 or MAXSIM_BF16 (Q and docs); other arguments as maxsim_rerank.
+ * Every call on one GPU shares that GPU's scratch and leaves its contents there: calls
+ * that overlap on one GPU (on different streams, or from several host threads before
+ * the earlier call's kernels finish) race and give wrong scores; the caller must
+ * serialise them, e.g. by issuing them all on one stream.
+ * Limit: the schedule must fit in the 64 MiB: 32 bytes per doc, plus the split docs'
+ * partial maxima, at most (8 W + min(B, 8 W)) slots of 4 bytes per padded query row (W
+ * the score launch's waves; about 6.3 MB at Lq 32 on MI355X, 8.5 MB for 256 docs at
+ * Lq 128), i.e. about 1.8 million docs at Lq <= 32. A larger batch returns
+ * MAXSIM_ERR_SCRATCH with nothing enqueued.
+ */
+MAXSIM_API int maxsim_rerank_noalloc(int dtype, const void *Q, int32_t Lq, int32_t d,
+                          const void *docs, int64_t stride,
+                          const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B,
+                          float *scores, void *stream);
 
 /*
  * Many queries in one launch ("pairs": each doc is scored against its own query).

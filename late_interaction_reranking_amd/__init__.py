@@ -31,6 +31,7 @@ from .maxsim import (  # noqa: F401
     maxsim_rerank_pairs_bf16,
     maxsim_rerank_pairs_fp8,
     maxsim_rerank_short,
+    maxsim_rerank_noalloc,
     maxsim_rerank_topk,
     maxsim_topk,
     maxsim_finish,

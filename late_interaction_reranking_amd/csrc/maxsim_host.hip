@@ -842,6 +842,60 @@ int with_workspace(hipStream_t s, size_t need, F &&enqueue)
     return rc;
 }
 
+// ---------------------------------------------------------------- static scratch
+//
+// maxsim_rerank_noalloc's workspace: a fixed array in device memory. Each GPU the
+// library runs on holds its own copy, at its own address, until the process ends. In
+// host code the array's name is only a stand-in for it, never an address: a GPU's copy
+// is reached through the pointer hipGetSymbolAddress returns, taken once per device with
+// that device current. Every call on a GPU shares that GPU's copy, so calls that overlap
+// on one GPU race (the caller serialises them). Nothing in it needs to start at zero:
+// the plan kernels write the header, the histogram rows and every descriptor before the
+// score and combine kernels read them, and a split doc's slots are written by its chunks
+// before the combine kernel reads them.
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+char *g_scratch_ptr[kMaxDevices];
+int g_scratch_status[kMaxDevices];
+
+int scratch_of_current_device(char **out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MAXSIM_ERR_HIP;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void *p = nullptr;
+        const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e == hipSuccess && p) {
+            g_scratch_ptr[dev] = static_cast<char *>(p);
+            g_scratch_status[dev] = MAXSIM_OK;
+        } else {
+            (void)hipGetLastError();
+            g_scratch_ptr[dev] = nullptr;
+            g_scratch_status[dev] = MAXSIM_ERR_HIP;
+        }
+    });
+    *out = g_scratch_ptr[dev];
+    return g_scratch_status[dev];
+}
+
+// Waves of the score launch of format fmt for (Lq, d): the grid launch_score uses
+// (CUs x resident workgroups of that instance x 4 waves), from the same occupancy query.
+int score_launch_waves(int fmt, int32_t Lq, int32_t d, uint32_t *waves)
+{
+    const Config c = choose_config(Lq, d);
+    if (c.lq_pad > kMaxLqPad || c.nqt * c.nks > kMaxFragsPerGroup) return MAXSIM_ERR_UNSUPPORTED;
+    const void *fn = score_fn(fmt, c);
+    if (!fn) return MAXSIM_ERR_UNSUPPORTED;
+    int per_cu = 0;
+    if (score_blocks_per_cu(fn, score_lds_bytes(c, d, fmt), &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    DeviceFacts f;
+    if (current_facts(&f) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    *waves = (uint32_t)(f.cus * per_cu * kScoreWaves);
+    return MAXSIM_OK;
+}
+
 // Plan, score and combine into the workspace w (layout L); qt.max_lq sizes the kernel
 // configuration.
 int enqueue_all(int fmt, const void *Q, const QueryTable &qt, int32_t d, const void *docs, int64_t stride,
@@ -877,6 +931,30 @@ int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, in
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     if (Lq == 0) return launch_fill(scores, B, 0.0f, stream);
     return run_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, stream);
+}
+
+// maxsim_rerank's plan, score and combine with the static scratch as the workspace. Its
+// partial-maxima slots are sized with the score launch's own wave count (the bound grows
+// with W, so the launch's W is enough), which keeps the schedule of a large batch well
+// inside the array.
+int rerank_noalloc(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                   const int32_t *offsets, const int32_t *lengths, int32_t B, float *scores, void *stream_ptr)
+{
+    if (dtype != MAXSIM_F16 && dtype != MAXSIM_BF16) return MAXSIM_ERR_INVALID_ARG;
+    const int st = check_common(Q, Lq, d, docs, stride, offsets, lengths, B, scores);
+    if (st != MAXSIM_OK) return st;
+    if (B == 0) return MAXSIM_OK;
+    hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
+    if (Lq == 0) return launch_fill(scores, B, 0.0f, stream);
+    uint32_t waves = 0;
+    int rc = score_launch_waves(dtype, Lq, d, &waves);
+    if (rc != MAXSIM_OK) return rc;
+    const Layout L = make_layout(choose_config(Lq, d).lq_pad, B, waves);
+    if (L.total > kScratchBytes) return MAXSIM_ERR_SCRATCH;
+    char *w = nullptr;
+    if ((rc = scratch_of_current_device(&w)) != MAXSIM_OK) return rc;
+    return enqueue_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, L, w,
+                       stream);
 }
 
 // A usable scale of FP8 docs: positive and at most 3.4e38 (so finite), never NaN. The
@@ -1185,6 +1263,13 @@ int maxsim_rerank_bf16(const void *Q, int32_t Lq, int32_t d, const void *docs, i
     return rerank(MAXSIM_BF16, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores, stream);
 }
 
+int maxsim_rerank_noalloc(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
+                          const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, float *scores,
+                          void *stream)
+{
+    return rerank_noalloc(dtype, Q, Lq, d, docs, stride, doc_offsets, doc_lengths, B, scores, stream);
+}
+
 int maxsim_rerank_short(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, int64_t stride,
                         const int32_t *doc_offsets, const int32_t *doc_lengths, int32_t B, float *scores,
                         void *stream)
@@ -1294,6 +1379,7 @@ const char *maxsim_status_string(int status)
     case MAXSIM_ERR_UNSUPPORTED: return "unsupported shape or alignment (need d <= 256 and d % 8 == 0, Lq <= 256, stride % 8 == 0 and <= 2^24, 16-byte aligned Q and docs)";
     case MAXSIM_ERR_HIP: return "HIP call failed (no device, allocation or launch failure)";
     case MAXSIM_ERR_WORKSPACE: return "workspace null, not 256-byte aligned, or too small";
+    case MAXSIM_ERR_SCRATCH: return "the batch needs more scratch than maxsim_rerank_noalloc's static 64 MiB per GPU holds";
     default: return "unknown status";
     }
 }

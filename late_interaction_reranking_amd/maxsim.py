@@ -65,6 +65,7 @@ __all__ = [
     "rerank",
     "maxsim_rerank_short",
     "rerank_short",
+    "maxsim_rerank_noalloc",
     "maxsim_rerank_pairs",
     "maxsim_rerank_pairs_bf16",
     "maxsim_plan_pairs",
@@ -123,6 +124,8 @@ def load() -> ctypes.CDLL:
             fn.argtypes = rr
         lib.maxsim_rerank_short.restype = ctypes.c_int
         lib.maxsim_rerank_short.argtypes = [ctypes.c_int, *rr]
+        lib.maxsim_rerank_noalloc.restype = ctypes.c_int
+        lib.maxsim_rerank_noalloc.argtypes = [ctypes.c_int, *rr]
         lib.maxsim_status_string.restype = ctypes.c_char_p
         lib.maxsim_status_string.argtypes = [ctypes.c_int]
         lib.maxsim_workspace_size.restype = ctypes.c_int
@@ -275,6 +278,23 @@ def maxsim_rerank_short(Q, docs, doc_offsets, doc_lengths, scores=None) -> torch
 
 
 rerank_short = maxsim_rerank_short
+
+
+def maxsim_rerank_noalloc(Q, docs, doc_offsets, doc_lengths, scores=None) -> torch.Tensor:
+    """maxsim_rerank's scores (bitwise) with the library's fixed per-GPU scratch as the
+    workspace: the call allocates no device memory (pass `scores` to allocate nothing
+    at all). Calls that overlap on one GPU race; fp16 or bf16 by Q's dtype."""
+    dtype = torch.bfloat16 if Q.dtype == torch.bfloat16 else torch.float16
+    Lq, d, stride, B = _marshal(Q, docs, doc_offsets, doc_lengths, dtype)
+    scores = _scores_out(scores, (B,), docs.device)
+    code = MAXSIM_BF16 if dtype == torch.bfloat16 else MAXSIM_F16
+    with torch.cuda.device(docs.device):
+        st = load().maxsim_rerank_noalloc(
+            code, Q.data_ptr(), Lq, d, docs.data_ptr(), stride, doc_offsets.data_ptr(),
+            doc_lengths.data_ptr(), B, scores.data_ptr(), _stream(docs),
+        )
+    _check(st, "maxsim_rerank_noalloc")
+    return scores
 
 
 def maxsim_workspace_size(Lq: int, d: int, B: int, device=None) -> int:

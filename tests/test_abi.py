@@ -37,6 +37,7 @@ def test_header_declares_the_boundary():
               "maxsim_rerank_fp8", "maxsim_rerank_fp8_bf16", "maxsim_score_fp8", "maxsim_finish_fp8",
               "maxsim_topk_workspace_size", "maxsim_topk", "maxsim_rerank_topk", "maxsim_rerank_topk_bf16",
               "maxsim_rerank_pairs_fp8", "maxsim_rerank_multi_fp8", "maxsim_rerank_short",
+              "maxsim_rerank_noalloc",
               "maxsim_rerank_short_fp8"):
         assert n in names
 
@@ -124,6 +125,40 @@ def call_short(lib, dtype=0, **kw):
 ])
 def test_short_validation(lib, kw, code):
     assert call_short(lib, **kw) == code
+
+
+def call_noalloc(lib, dtype=0, **kw):
+    args = dict(Q=FAKE, Lq=32, d=128, docs=FAKE, stride=128, offs=FAKE, lens=FAKE + 1024, B=10,
+                scores=FAKE + 4096)
+    args.update(kw)
+    return lib.maxsim_rerank_noalloc(dtype, args["Q"], args["Lq"], args["d"], args["docs"], args["stride"],
+                                     args["offs"], args["lens"], args["B"], args["scores"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=2), INVALID),
+    (dict(dtype=-1), INVALID),
+    (dict(B=-1), INVALID),
+    (dict(Lq=-1), INVALID),
+    (dict(stride=64), INVALID),
+    (dict(scores=None), INVALID),
+    (dict(docs=None), INVALID),
+    (dict(offs=FAKE + 2), INVALID),
+    (dict(d=12, stride=16), UNSUPPORTED),
+    (dict(Lq=257), UNSUPPORTED),
+    (dict(Q=FAKE + 4), UNSUPPORTED),
+    (dict(stride=(1 << 24) + 8), UNSUPPORTED),
+    (dict(B=0, docs=None, offs=None, lens=None, scores=None), OK),
+    (dict(dtype=1, B=0, docs=None, offs=None, lens=None, scores=None), OK),
+])
+def test_noalloc_validation(lib, kw, code):
+    """maxsim_rerank_noalloc checks its arguments on the host, as maxsim_rerank does,
+    before it touches the GPU or its scratch."""
+    assert call_noalloc(lib, **kw) == code
+
+
+def test_scratch_status_string(lib):
+    assert "64 MiB" in lir.maxsim_status_string(5)
 
 
 def call_short_fp8(lib, dtype=0, scale=1.0, **kw):
