@@ -419,6 +419,12 @@ def main() -> int:
     ap.add_argument("--short", action="store_true",
                     help="single-query workloads: one launch per step, one workgroup per doc "
                          "(maxsim_rerank_short) instead of plan + score + combine")
+    ap.add_argument("--path", choices=["staged", "one-shot"], default="staged",
+                    help="single-query workloads: 'staged' times maxsim_plan, maxsim_score and "
+                         "maxsim_finish on a caller workspace (events around the score kernel); "
+                         "'one-shot' times maxsim_rerank (maxsim_rerank_fp8) itself, events around the "
+                         "whole call: for at most 1024 docs the self-scheduling range kernel and its "
+                         "combine, else plan, score and combine")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of one step captured in a HIP graph (no host "
                          "launch cost per kernel); the per-launch roofline still comes from eager steps")
@@ -489,6 +495,10 @@ def main() -> int:
     if args.short and (w.shared_docs or w.multi_query or args.topk):
         print("--short applies to single-query workloads without --topk", file=sys.stderr)
         return 2
+    one_shot_path = args.path == "one-shot"
+    if one_shot_path and (w.shared_docs or w.multi_query or args.topk or args.short):
+        print("--path one-shot applies to single-query workloads without --topk or --short", file=sys.stderr)
+        return 2
     if args.topk:
         if w.shared_docs or w.multi_query:
             print("--topk applies to single-query workloads", file=sys.stderr)
@@ -502,7 +512,7 @@ def main() -> int:
     log("uploaded")
     tk_events = []
 
-    def step(ev_a=None, ev_b=None):
+    def step(ev_a=None, ev_b=None, force_staged=False):
         if w.shared_docs:
             if ev_a is not None:
                 ev_a.record()
@@ -510,6 +520,16 @@ def main() -> int:
                 lir.maxsim_rerank_multi_fp8(Q, q_lengths, X, offs, lens, w.doc_scale, scores=scores)
             else:
                 lir.rerank_multi(Q, q_lengths, X, offs, lens, scores=scores)
+            if ev_b is not None:
+                ev_b.record()
+            return
+        if one_shot_path and not force_staged:
+            if ev_a is not None:
+                ev_a.record()
+            if w.X8 is not None:
+                lir.maxsim_rerank_fp8(Q, X, offs, lens, w.doc_scale, scores=scores)
+            else:
+                lir.rerank(Q, X, offs, lens, scores=scores)
             if ev_b is not None:
                 ev_b.record()
             return
@@ -576,17 +596,31 @@ def main() -> int:
         flush_reps = 200 if w.doc_bytes < 100e6 else (50 if w.doc_bytes < 1e9 else 20)
     flushed = None
     if flush_reps > 0:
+        # Two passes, so that each timed interval holds as few event markers as possible
+        # (a marker costs microseconds of GPU time): the whole step, then (staged path)
+        # the score kernel alone. After each evicting write an untimed marker comes first,
+        # so that the write's completion is not charged to the step.
         evict = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        fl = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(4)) for _ in range(flush_reps)]
+        pad = torch.cuda.Event()
+        fl = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(2)) for _ in range(flush_reps)]
         torch.cuda.synchronize()
-        for i, (s0, a, b, s1) in enumerate(fl):
+        for i, (s0, s1) in enumerate(fl):
             evict.fill_(i & 255)
+            pad.record()
             s0.record()
-            step(a, b)
+            step()
             s1.record()
         torch.cuda.synchronize()
-        f_step = [s0.elapsed_time(s1) for s0, _, _, s1 in fl]
-        f_score = [a.elapsed_time(b) for _, a, b, _ in fl]
+        f_step = [s0.elapsed_time(s1) for s0, s1 in fl]
+        if one_shot_path or args.short or w.shared_docs:
+            f_score = f_step  # the step is one call, bracketed by the same events
+        else:
+            for i, (a, b) in enumerate(fl):
+                evict.fill_(i & 255)
+                pad.record()
+                step(a, b)
+            torch.cuda.synchronize()
+            f_score = [a.elapsed_time(b) for a, b in fl]
         del evict
         flushed = {"reps": flush_reps, "evict_bytes": 1 << 30,
                    "step_ms": percentiles(f_step), "score_ms": percentiles(f_score)}
@@ -627,7 +661,7 @@ def main() -> int:
 
     one_shot = None
     if args.one_shot:
-        one_shot = time_one_shot(w, lir, Q, X, offs, lens, scores, ws, step, dev, args)
+        one_shot = time_one_shot(w, lir, Q, X, offs, lens, scores, ws, lambda: step(force_staged=True), dev, args)
         log(f"one-shot: {one_shot['call_us']['median']:.1f} us per synced call, staged "
             f"{one_shot['staged_us']['median']:.1f} us (ratio {one_shot['ratio_median']:.2f})")
 
@@ -674,7 +708,9 @@ def main() -> int:
         "launch": ("HIP graph replay of one captured step" if args.graph
                    else "eager: one host launch per kernel"),
         "path": ("one launch, one workgroup per doc (maxsim_rerank_short)" if args.short
-                 else "scheduled: plan, score, combine"),
+                 else (("one-shot maxsim_rerank: self-scheduling range kernel + combine" if w.B <= 1024
+                        else "one-shot maxsim_rerank: plan, score, combine") if one_shot_path
+                       else "scheduled: plan, score, combine")),
         "ms_per_step_eager": ms_per_step_eager,
         "value_counts": ("each (query, doc token) pair once" if w.shared_docs else "each doc token once"),
         "hbm_GBps_step": alg_bytes / (ms_per_step * 1e-3) / 1e9,
@@ -684,12 +720,14 @@ def main() -> int:
             "bound": "hbm",
             "kernel": ("score_kernel (per pass: the maxsim_rerank_multi call's time, plan and combines "
                        "included, over its score launches)" if w.shared_docs
-                       else ("short_kernel" if args.short else "score_kernel")),
+                       else ("short_kernel" if args.short else
+                             ("whole maxsim_rerank call (every kernel of the step)" if one_shot_path
+                              else "score_kernel"))),
             "achieved": achieved,
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": achieved / HBM_PEAK_GBPS,
-            "traffic": None if args.short else measured_traffic(w.name),
+            "traffic": None if (args.short or one_shot_path) else measured_traffic(w.name),
             "algorithmic_bytes_per_launch": launch_bytes,
             "avg_launch_ms": launch_ms,
             "launches_per_step": launches,

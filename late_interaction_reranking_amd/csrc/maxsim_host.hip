@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "maxsim_common.h"
+#include "maxsim_range.h"
 #include "maxsim_sched.h"
 #include "maxsim_topk.h"
 
@@ -75,6 +76,36 @@ MAXSIM_DECLARE_SHORT(bf16)
 MAXSIM_DECLARE_SHORT(f16_fp8)
 MAXSIM_DECLARE_SHORT(bf16_fp8)
 #undef MAXSIM_DECLARE_SHORT
+
+// Self-scheduling range kernels (small single-query batches), one lookup per file.
+#define MAXSIM_DECLARE_RANGE(fmt)                                                   \
+    const void *maxsim_range_kernel_##fmt##_k1(int);                               \
+    const void *maxsim_range_kernel_##fmt##_k2(int);                               \
+    const void *maxsim_range_kernel_##fmt##_k3(int);                               \
+    const void *maxsim_range_kernel_##fmt##_k4(int);                               \
+    const void *maxsim_range_kernel_##fmt##_k5(int);                               \
+    const void *maxsim_range_kernel_##fmt##_k6(int);                               \
+    const void *maxsim_range_kernel_##fmt##_k7(int);                               \
+    const void *maxsim_range_kernel_##fmt##_k8(int);                               \
+    const void *maxsim_range_kernel_##fmt(int nks, int nqt)                        \
+    {                                                                              \
+        switch (nks) {                                                             \
+        case 1: return maxsim_range_kernel_##fmt##_k1(nqt);                        \
+        case 2: return maxsim_range_kernel_##fmt##_k2(nqt);                        \
+        case 3: return maxsim_range_kernel_##fmt##_k3(nqt);                        \
+        case 4: return maxsim_range_kernel_##fmt##_k4(nqt);                        \
+        case 5: return maxsim_range_kernel_##fmt##_k5(nqt);                        \
+        case 6: return maxsim_range_kernel_##fmt##_k6(nqt);                        \
+        case 7: return maxsim_range_kernel_##fmt##_k7(nqt);                        \
+        case 8: return maxsim_range_kernel_##fmt##_k8(nqt);                        \
+        default: return nullptr;                                                   \
+        }                                                                          \
+    }
+MAXSIM_DECLARE_RANGE(f16)
+MAXSIM_DECLARE_RANGE(bf16)
+MAXSIM_DECLARE_RANGE(f16_fp8)
+MAXSIM_DECLARE_RANGE(bf16_fp8)
+#undef MAXSIM_DECLARE_RANGE
 
 namespace {
 
@@ -448,6 +479,92 @@ combine_kernel(const CombineArgs a)
         wave_lds_sync();
     }
 }
+
+}  // namespace
+
+namespace maxsim {
+
+// Scores of the docs a range launch split (csrc/maxsim_range.h): one wave per doc. Doc
+// i's pieces are the tail slot of the wave holding its first tile and the head slots of
+// the following waves up to the one holding its last tile; their max is exact, and the
+// sum runs in the score kernel's fixed order (query tiles ascending, then lanes 0, 16,
+// 32, 48), so the score is bitwise the one an unsplit doc gets.
+__global__ void __launch_bounds__(kScoreBlock)
+range_combine_kernel(const RangeCombineArgs a)
+{
+    __shared__ f32x4 s_red[kScoreBlock];
+    __shared__ f32x4 s_quad[kScoreWaves][kMaxQuads];
+    const unsigned long long T = a.scan[a.B];
+    if (T == 0ull) return;  // every doc empty: no pieces
+    const uint32_t wact = range_active_waves(T, a.waves);
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    const int kgroup = lane >> 4;
+    const int lq_pad = a.nqt * kTileRows;
+    const int nquads = lq_pad / 4;
+    const uint32_t S = (uint32_t)(kWave / nquads);
+    const int quad = lane % nquads;
+    const uint32_t sl = (uint32_t)(lane / nquads);
+    f32x4 *red = s_red + wave * kWave;
+    f32x4 *rq = s_quad[wave];
+    constexpr float NEG_INF = -__builtin_huge_valf();
+    for (int di = (int)blockIdx.x * kScoreWaves + wave; di < a.B; di += (int)gridDim.x * kScoreWaves) {
+        typedef __attribute__((address_space(4))) const unsigned long long ConstU64;
+        const unsigned long long s = ((ConstU64 *)a.scan)[di];
+        const unsigned long long e = ((ConstU64 *)a.scan)[di + 1];
+        if (e == s) continue;
+        const uint32_t w_lo = range_wave(s, T, wact);
+        const uint32_t w_hi = range_wave(e - 1ull, T, wact);
+        if (w_lo == w_hi) continue;
+        const uint32_t K = w_hi - w_lo + 1u;
+        // Piece k's slot: the tail slot of wave w_lo for k = 0, else the head slot of wave
+        // w_lo + k. Eight loads in flight per lane before their max.
+        constexpr int U = 8;
+        f32x4 m = {NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+        if (sl < S) {
+            for (uint32_t k0 = sl; k0 < K; k0 += U * S) {
+                f32x4 v[U];
+#pragma unroll
+                for (int u = 0; u < U; ++u) {
+                    const uint32_t k = k0 + u * S;
+                    const uint32_t slot = k == 0u ? wact + w_lo : w_lo + k;
+                    v[u] = k < K ? *reinterpret_cast<const f32x4 *>(a.partials + (size_t)slot * lq_pad + quad * 4)
+                                 : f32x4{NEG_INF, NEG_INF, NEG_INF, NEG_INF};
+                }
+#pragma unroll
+                for (int u = 0; u < U; ++u) m = max4(m, v[u]);
+            }
+        }
+        red[lane] = m;
+        wave_lds_sync();
+        if (lane < nquads) {
+            f32x4 r = red[lane];
+            for (uint32_t k = 1; k < S; ++k) r = max4(r, red[k * nquads + lane]);
+            rq[lane] = r;
+        }
+        wave_lds_sync();
+        float lane_sum = 0.0f;
+        for (int t = 0; t < a.nqt; ++t) {
+            const int left = a.Lq - t * kTileRows;
+            const int nr = left < 0 ? 0 : (left > kTileRows ? kTileRows : left);
+            const f32x4 v = rq[t * 4 + kgroup];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) lane_sum += kgroup * 4 + i < nr ? v[i] : 0.0f;
+        }
+        const int ls = __builtin_bit_cast(int, lane_sum);
+        const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 0));
+        const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 16));
+        const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 32));
+        const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
+        const float sum = (((s0 + s1) + s2) + s3) * a.doc_scale;
+        if (lane == 0) a.scores[di] = sum;
+        wave_lds_sync();
+    }
+}
+
+}  // namespace maxsim
+
+namespace {
 
 __global__ void fill_kernel(float *__restrict__ out, int32_t n, float v)
 {
@@ -896,6 +1013,106 @@ int score_launch_waves(int fmt, int32_t Lq, int32_t d, uint32_t *waves)
     return MAXSIM_OK;
 }
 
+// ---------------------------------------------------------------- range launches
+//
+// A single-query batch of at most kRangeMaxDocs docs whose query fits one register group
+// runs as two launches: the self-scheduling range kernel (csrc/maxsim_range.h), which
+// cuts the docs' tiles into equal contiguous ranges per wave, and range_combine_kernel
+// for the docs it split. No plan launch. Its workspace holds the tile prefix sums (the
+// last is the tile total) and 2 W slots of per-row maxima.
+bool range_eligible(int32_t Lq, int32_t d, int32_t B)
+{
+    if (B < 1 || B > kRangeMaxDocs || Lq < 1) return false;
+    return choose_config(Lq, d).ngroups == 1;
+}
+
+const void *range_fn(int fmt, const Config &c)
+{
+    switch (fmt) {
+    case MAXSIM_F16: return maxsim_range_kernel_f16(c.nks, c.nqt);
+    case MAXSIM_BF16: return maxsim_range_kernel_bf16(c.nks, c.nqt);
+    case MAXSIM_F16 | kFmtFp8Docs: return maxsim_range_kernel_f16_fp8(c.nks, c.nqt);
+    case MAXSIM_BF16 | kFmtFp8Docs: return maxsim_range_kernel_bf16_fp8(c.nks, c.nqt);
+    default: return nullptr;
+    }
+}
+
+// Dynamic LDS: the query tile and, after it, the prologue's prefix sums; then the same
+// tile slots as the score kernel, over both.
+size_t range_scan_lds(const Config &c) { return (q_lds_bytes(c) + 15) & ~size_t(15); }
+
+size_t range_lds_bytes(const Config &c, int fmt)
+{
+    const bool fp8 = (fmt & kFmtFp8Docs) != 0;
+    const size_t q = range_scan_lds(c) + kRangePrologueBytes;
+    const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt, fp8) * dma_tile_bytes(c.nks, fp8);
+    return q > slots ? q : slots;
+}
+
+struct RangePlan {
+    const void *fn;
+    size_t lds;
+    uint32_t blocks;
+    size_t scan, partials, bytes;  // workspace layout
+};
+
+int range_plan(int fmt, int32_t Lq, int32_t d, int32_t B, RangePlan *rp)
+{
+    const Config c = choose_config(Lq, d);
+    if (c.ngroups != 1 || c.nqt * c.nks > kMaxFragsPerGroup) return MAXSIM_ERR_UNSUPPORTED;
+    rp->fn = range_fn(fmt, c);
+    if (!rp->fn) return MAXSIM_ERR_UNSUPPORTED;
+    rp->lds = range_lds_bytes(c, fmt);
+    int per_cu = 0;
+    if (score_blocks_per_cu(rp->fn, rp->lds, &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    DeviceFacts f;
+    if (current_facts(&f) != MAXSIM_OK) return MAXSIM_ERR_HIP;
+    rp->blocks = (uint32_t)(f.cus * per_cu);
+    const size_t waves = (size_t)rp->blocks * kScoreWaves;
+    rp->scan = 0;
+    rp->partials = align256((size_t)8 * (B + 1));
+    rp->bytes = align256(rp->partials + 2 * waves * (size_t)c.lq_pad * 4);
+    return MAXSIM_OK;
+}
+
+int enqueue_range(int fmt, const RangePlan &rp, const void *Q, int32_t Lq, int32_t d, const void *docs,
+                  int64_t stride, const int32_t *offsets, const int32_t *lengths, int32_t B, float *scores,
+                  float doc_scale, char *w, hipStream_t stream)
+{
+    const Config c = choose_config(Lq, d);
+    const bool fp8 = (fmt & kFmtFp8Docs) != 0;
+    RangeArgs a;
+    a.Q = static_cast<const uint16_t *>(Q);
+    a.docs = static_cast<const char *>(docs);
+    a.stride_bytes = stride * (fp8 ? 1 : 2);
+    a.offsets = offsets;
+    a.lengths = lengths;
+    a.scores = scores;
+    a.scan = reinterpret_cast<unsigned long long *>(w + rp.scan);
+    a.partials = reinterpret_cast<float *>(w + rp.partials);
+    a.B = B;
+    a.d = d;
+    a.Lq = Lq;
+    a.scan_lds = (uint32_t)range_scan_lds(c);
+    a.doc_scale = fp8 ? doc_scale : 1.0f;
+    void *args[] = {&a};
+    if (hipLaunchKernel(rp.fn, dim3(rp.blocks), dim3(kScoreBlock), args, rp.lds, stream) != hipSuccess)
+        return MAXSIM_ERR_HIP;
+    if (hipGetLastError() != hipSuccess) return MAXSIM_ERR_HIP;
+    RangeCombineArgs ca;
+    ca.scan = a.scan;
+    ca.partials = a.partials;
+    ca.scores = scores;
+    ca.B = B;
+    ca.Lq = Lq;
+    ca.nqt = c.nqt;
+    ca.waves = rp.blocks * kScoreWaves;
+    ca.doc_scale = a.doc_scale;
+    hipLaunchKernelGGL(range_combine_kernel, dim3((unsigned)((B + kScoreWaves - 1) / kScoreWaves)),
+                       dim3(kScoreBlock), 0, stream, ca);
+    return hipGetLastError() == hipSuccess ? MAXSIM_OK : MAXSIM_ERR_HIP;
+}
+
 // Plan, score and combine into the workspace w (layout L); qt.max_lq sizes the kernel
 // configuration.
 int enqueue_all(int fmt, const void *Q, const QueryTable &qt, int32_t d, const void *docs, int64_t stride,
@@ -930,6 +1147,14 @@ int rerank(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs, in
     if (B == 0) return MAXSIM_OK;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     if (Lq == 0) return launch_fill(scores, B, 0.0f, stream);
+    if (range_eligible(Lq, d, B)) {
+        RangePlan rp;
+        const int rc = range_plan(dtype, Lq, d, B, &rp);
+        if (rc != MAXSIM_OK) return rc;
+        return with_workspace(stream, rp.bytes, [&](char *w) {
+            return enqueue_range(dtype, rp, Q, Lq, d, docs, stride, offsets, lengths, B, scores, 1.0f, w, stream);
+        });
+    }
     return run_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, stream);
 }
 
@@ -946,6 +1171,15 @@ int rerank_noalloc(int dtype, const void *Q, int32_t Lq, int32_t d, const void *
     if (B == 0) return MAXSIM_OK;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     if (Lq == 0) return launch_fill(scores, B, 0.0f, stream);
+    if (range_eligible(Lq, d, B)) {
+        RangePlan rp;
+        int rc = range_plan(dtype, Lq, d, B, &rp);
+        if (rc != MAXSIM_OK) return rc;
+        if (rp.bytes > kScratchBytes) return MAXSIM_ERR_SCRATCH;
+        char *w = nullptr;
+        if ((rc = scratch_of_current_device(&w)) != MAXSIM_OK) return rc;
+        return enqueue_range(dtype, rp, Q, Lq, d, docs, stride, offsets, lengths, B, scores, 1.0f, w, stream);
+    }
     uint32_t waves = 0;
     int rc = score_launch_waves(dtype, Lq, d, &waves);
     if (rc != MAXSIM_OK) return rc;
@@ -1042,11 +1276,18 @@ int rerank_topk(int dtype, const void *Q, int32_t Lq, int32_t d, const void *doc
     if (st != MAXSIM_OK) return st;
     if (k == 0) return MAXSIM_OK;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
-    // Workspace: rerank layout (when there is one), then the scores, then the top-k's.
+    // Workspace: the rerank's (when there is one), then the scores, then the top-k's.
     Layout L{};
+    RangePlan rp{};
     const bool ranked = B > 0 && Lq > 0;
-    if (ranked && workspace_layout(Lq, d, B, &L) != MAXSIM_OK) return MAXSIM_ERR_HIP;
-    const size_t score_at = ranked ? L.total : 0;
+    const bool ranged = ranked && range_eligible(Lq, d, B);
+    if (ranged) {
+        const int rc = range_plan(dtype, Lq, d, B, &rp);
+        if (rc != MAXSIM_OK) return rc;
+    } else if (ranked && workspace_layout(Lq, d, B, &L) != MAXSIM_OK) {
+        return MAXSIM_ERR_HIP;
+    }
+    const size_t score_at = ranged ? rp.bytes : (ranked ? L.total : 0);
     const size_t score_bytes = ((size_t)(B > 0 ? B : 1) * 4 + 255) & ~size_t(255);
     const size_t need = score_at + score_bytes + topk_workspace_bytes(B, k);
     return with_workspace(stream, need, [&](char *w) {
@@ -1055,6 +1296,8 @@ int rerank_topk(int dtype, const void *Q, int32_t Lq, int32_t d, const void *doc
         if (B > 0) {
             if (!ranked)
                 rc = launch_fill(scores, B, 0.0f, stream);
+            else if (ranged)
+                rc = enqueue_range(dtype, rp, Q, Lq, d, docs, stride, offsets, lengths, B, scores, 1.0f, w, stream);
             else
                 rc = enqueue_all(dtype, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores, 1.0f, L,
                                  w, stream);
@@ -1074,6 +1317,15 @@ int rerank_fp8(int dtype, const void *Q, int32_t Lq, int32_t d, const void *docs
     if (B == 0) return MAXSIM_OK;
     hipStream_t stream = static_cast<hipStream_t>(stream_ptr);
     if (Lq == 0) return launch_fill(scores, B, 0.0f, stream);
+    if (range_eligible(Lq, d, B)) {
+        RangePlan rp;
+        const int rc = range_plan(dtype | kFmtFp8Docs, Lq, d, B, &rp);
+        if (rc != MAXSIM_OK) return rc;
+        return with_workspace(stream, rp.bytes, [&](char *w) {
+            return enqueue_range(dtype | kFmtFp8Docs, rp, Q, Lq, d, docs, stride, offsets, lengths, B, scores,
+                                 doc_scale, w, stream);
+        });
+    }
     return run_all(dtype | kFmtFp8Docs, Q, single_query(Lq), d, docs, stride, offsets, lengths, B, scores,
                    doc_scale, stream);
 }

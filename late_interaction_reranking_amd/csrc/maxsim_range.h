@@ -1,0 +1,454 @@
+// MaxSim score kernel for small single-query batches (at most kRangeMaxDocs docs, one
+// register group of query tiles) that schedules itself: one launch, no plan launch.
+//
+// Operation (Flash-MaxSim rerank page, docs.vllm.ai,
+// vllm.v1.pool.flash_maxsim.flash_maxsim_rerank, module description and section
+// `_maxsim_rerank_kernel`): score_i = sum over query rows q of the max over doc i's rows
+// t of Q[q] . X[off_i + t], fp16/bf16 inputs, fp32 products and sums.
+//
+// Schedule. The docs' 16-row tiles, taken in doc index order, form one sequence of T
+// tiles: doc i holds tiles [S_i, S_i + nt_i), nt_i = ceil(len_i / 16), S the exclusive
+// prefix sums. It is cut into W_act ranges of equal size (to one tile): wave w takes
+// tiles [floor(w T / W_act), floor((w + 1) T / W_act)), W_act = min(W, T / kMinRangeTiles)
+// (at least 1). Every workgroup loads the lengths and forms S in LDS itself, so nothing
+// runs before this launch, and the balance is exact: with a few tiles per wave, a deal
+// of whole docs or of chunks leaves the slowest wave about twice the average.
+//
+// Pieces. A wave's range holds whole docs and, at its two ends, pieces of docs that
+// other waves also cover. A whole doc is summed and stored here, as the score kernel
+// does. A piece stores its per-row maxima in a slot: the piece that opens the range (a
+// doc begun by an earlier wave) in head slot w, the piece that closes it (a doc that a
+// later wave continues) in tail slot W_act + w. range_combine_kernel then finds a split
+// doc's pieces by the same arithmetic (the tail slot of the wave holding its first tile,
+// the head slots of the next waves up to the one holding its last tile), takes the max
+// (exact, order-free) and sums in the same fixed order, so the score is bitwise the one
+// any other schedule gives.
+//
+// Pipeline. Each wave runs its range as one stream of tiles through P LDS-DMA slots
+// (the score kernel's slot layout, fragments and running max). The issue side walks the
+// docs P tiles ahead of the consume side and leaves, per slot, what the consume side
+// needs: the tile's valid rows, whether it ends a piece, and the piece's doc and slot.
+// Doc boundaries therefore cost no pipeline bubble. The doc lengths and offsets come
+// from a window of 64 docs held one per lane; only the prologue needs S, which it keeps
+// in the LDS that the tile slots take over afterwards. Tile positions are 64-bit: docs
+// may overlap, so T is bounded only by B * 2^27.
+#pragma once
+
+#include "maxsim_score.h"
+
+namespace maxsim {
+
+constexpr int kRangeMaxDocs = 1024;           // docs of a range launch: 4 per thread
+constexpr uint32_t kMinRangeTiles = 2;        // fewest tiles per active wave
+// LDS of the prologue, after the query tile: S (64-bit, B + 1 entries), then the lengths
+// and offsets (32-bit, B each). The tile slots take it over once the waves have their
+// first docs.
+constexpr size_t kRangeScanBytes = 8 * (kRangeMaxDocs + 2);
+constexpr size_t kRangePrologueBytes = kRangeScanBytes + 8 * kRangeMaxDocs;
+
+struct RangeArgs {
+    const uint16_t *Q;             // [Lq, d]
+    const char *docs;              // row r at docs + r * stride_bytes
+    int64_t stride_bytes;
+    const int32_t *offsets;        // [B]
+    const int32_t *lengths;        // [B]
+    float *scores;                 // [B]
+    unsigned long long *scan;      // workspace: S_0 .. S_B (S_B = T) for the combine kernel
+    float *partials;               // workspace: [2 W][16 NQT] head slots, then tail slots
+    int32_t B, d, Lq;
+    uint32_t scan_lds;             // byte offset of S in the dynamic LDS (after the query tile)
+    float doc_scale;               // FP8 docs: multiplies each sum (unused otherwise)
+};
+
+struct RangeCombineArgs {
+    const unsigned long long *scan;
+    const float *partials;
+    float *scores;
+    int32_t B, Lq, nqt;
+    uint32_t waves;                // W of the range launch
+    float doc_scale;
+};
+
+// Wave w's first tile when T tiles are cut into W_act ranges (T < 2^37, w < 2^16: the
+// products stay below 2^64).
+__host__ __device__ inline unsigned long long range_start(uint32_t w, unsigned long long T, uint32_t wact)
+{
+    return ((unsigned long long)w * T) / wact;
+}
+
+// The wave whose range holds tile t (t < T): the largest w with range_start(w) <= t.
+__host__ __device__ inline uint32_t range_wave(unsigned long long t, unsigned long long T, uint32_t wact)
+{
+    return (uint32_t)(((t + 1ull) * wact + T - 1ull) / T) - 1u;
+}
+
+__host__ __device__ inline uint32_t range_active_waves(unsigned long long T, uint32_t waves)
+{
+    unsigned long long w = T / kMinRangeTiles;
+    if (w < 1) w = 1;
+    return w < waves ? (uint32_t)w : waves;
+}
+
+template <int NKS, int NQT, bool BF16, bool FP8D, int P, int MINW>
+__global__ void __launch_bounds__(kScoreBlock, MINW)
+range_kernel(const RangeArgs a)
+{
+    constexpr int DPAD = NKS * kStepK;
+    constexpr int LDQ = DPAD + 8;                 // Q row pitch in LDS (halves), as the score kernel's
+    constexpr int CP = dma_row_chunks(NKS, FP8D);
+    constexpr int NLDD = CP / 4;
+    constexpr int TILE_CHUNKS = kTileRows * CP;
+    constexpr int LQP = NQT * kTileRows;          // padded query rows
+    constexpr float NEG_INF = -__builtin_huge_valf();
+
+    extern __shared__ __attribute__((aligned(16))) uint16_t qs[];  // Q tile | S; then the tile slots
+    __shared__ unsigned long long wave_tiles[kScoreWaves];
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = (int)wave_uniform(threadIdx.x / kWave);
+    const int row_in_tile = lane & 15;
+    const int kgroup = lane >> 4;
+    const uint32_t W = gridDim.x * kScoreWaves;
+    const uint32_t wid = blockIdx.x * kScoreWaves + wave;
+    const int B = a.B;
+    unsigned long long *S = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(qs) + a.scan_lds);
+
+    int32_t *lds_len = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(S) + kRangeScanBytes);
+    int32_t *lds_off = lds_len + kRangeMaxDocs;
+
+    // ---- prologue: lengths and offsets (4 docs per thread, one round of loads with the
+    // query tile's), tile counts and S
+    int32_t len4[4], off4[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int i = 4 * (int)threadIdx.x + j;
+        len4[j] = i < B ? a.lengths[i] : 0;
+        off4[j] = i < B ? a.offsets[i] : 0;
+    }
+    {
+        constexpr int CPR = DPAD / 8;
+        for (int e = threadIdx.x; e < LQP * CPR; e += kScoreBlock) {
+            const int r = e / CPR;
+            const int c = e - r * CPR;
+            u32x4 v = {0u, 0u, 0u, 0u};
+            if (r < a.Lq && c * 8 < a.d) v = *reinterpret_cast<const u32x4 *>(a.Q + (size_t)r * a.d + c * 8);
+            *reinterpret_cast<u32x4 *>(qs + r * LDQ + c * 8) = v;
+        }
+    }
+    uint32_t nt4[4];
+    unsigned long long mine = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        nt4[j] = len4[j] > 0 ? ((uint32_t)len4[j] + (kTileRows - 1)) / kTileRows : 0u;
+        mine += nt4[j];
+    }
+    // inclusive scan of the per-thread totals across the wave, then across the waves
+    unsigned long long incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const unsigned long long up = __shfl_up(incl, o);
+        if (lane >= o) incl += up;
+    }
+    if (lane == kWave - 1) wave_tiles[wave] = incl;
+    __syncthreads();
+    unsigned long long before = incl - mine, T = 0;
+#pragma unroll
+    for (int v = 0; v < kScoreWaves; ++v) {
+        const unsigned long long t = wave_tiles[v];
+        if (v < wave) before += t;
+        T += t;
+    }
+    {
+        unsigned long long s = before;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = 4 * (int)threadIdx.x + j;
+            if (i < B) {
+                S[i] = s;
+                lds_len[i] = len4[j];
+                lds_off[i] = off4[j];
+            }
+            s += nt4[j];
+        }
+        if (threadIdx.x == 0) S[B] = T;
+    }
+    if (blockIdx.x == 0) {
+        // For the combine kernel: S, with S_B = T; and -inf for empty docs (no tile, so
+        // no piece and no combine).
+        unsigned long long s = before;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int i = 4 * (int)threadIdx.x + j;
+            if (i < B) {
+                a.scan[i] = s;
+                if (nt4[j] == 0u) a.scores[i] = NEG_INF;
+            }
+            s += nt4[j];
+        }
+        if (threadIdx.x == 0) a.scan[B] = T;
+    }
+    __syncthreads();
+
+    // ---- this wave's range and its first doc (largest i with S_i <= first tile)
+    const uint32_t wact = range_active_waves(T, W);
+    unsigned long long r_begin = 0, r_end = 0;
+    if (wid < wact) {
+        r_begin = range_start(wid, T, wact);
+        r_end = wid + 1 == wact ? T : range_start(wid + 1, T, wact);
+    }
+    int first_doc = 0;
+    unsigned long long first_tile = 0;  // S of first_doc
+    if (r_end > r_begin) {
+        int lo = 0, hi = B;  // S[lo] <= r_begin < S[hi]
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (S[mid] <= r_begin) lo = mid;
+            else hi = mid;
+        }
+        first_doc = lo;
+        first_tile = S[lo];
+    }
+    first_doc = (int)wave_uniform((uint32_t)first_doc);
+    first_tile = wave_uniform64(first_tile);
+    r_begin = wave_uniform64(r_begin);
+    r_end = wave_uniform64(r_end);
+    // The first window of doc lengths and offsets (doc first_doc + l in lane l), from LDS.
+    int32_t wlen = 0, woff = 0;
+    if (first_doc + lane < B) {
+        wlen = lds_len[first_doc + lane];
+        woff = lds_off[first_doc + lane];
+    }
+
+    u32x4 qf[NQT][NKS];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+        for (int s = 0; s < NKS; ++s)
+            qf[qt][s] = *reinterpret_cast<const u32x4 *>(qs + (qt * kTileRows + row_in_tile) * LDQ + (s * 4 + kgroup) * 8);
+    __syncthreads();  // the tile slots now reuse the query's LDS (and the prologue's)
+
+    // ---- LDS-DMA slots and fragment addresses (the score kernel's layout)
+    const uint32_t stride_bytes = (uint32_t)a.stride_bytes;
+    const uint32_t tile_bytes = (uint32_t)kTileRows * stride_bytes;
+    const int C = FP8D ? a.d / 16 : a.d / 8;  // 16-byte chunks per doc row
+    u32x4 *const slots = reinterpret_cast<u32x4 *>(qs) + wave * (P * TILE_CHUNKS);
+    uint32_t dma_off[NLDD];
+#pragma unroll
+    for (int s = 0; s < NLDD; ++s) {
+        const int q = s * kWave + lane;
+        const int row = q / CP;
+        const int c = (q % CP) ^ dma_swizzle(row, CP);
+        dma_off[s] = c < C ? (uint32_t)row * stride_bytes + (uint32_t)c * 16u : (uint32_t)kTileRows * stride_bytes;
+    }
+    int rd_dma[NKS];
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+        const int c = FP8D ? (kgroup >> 1) + 2 * s : kgroup + 4 * s;
+        rd_dma[s] = row_in_tile * CP + (c ^ dma_swizzle(row_in_tile, CP));
+    }
+    const int rd_half = (kgroup & 1) * 8;
+
+    // ---- doc lengths and offsets: a window of 64 docs, doc win + l in lane l; later
+    // windows come from global memory
+    int win = first_doc;
+    auto load_window = [&](int base) {
+        win = base;
+        const int i = base + lane;
+        wlen = i < B ? a.lengths[i] : 0;
+        woff = i < B ? a.offsets[i] : 0;
+        // Waited for here, on this path alone: otherwise the compiler's wait analysis
+        // would make every later pass of the tile loop wait for all loads in flight.
+        __builtin_amdgcn_s_waitcnt(kWaitAllVmem);
+    };
+    // Length and offset of doc j (wave-uniform): from the window, moved forward when j
+    // leaves it (the walk only moves forward).
+    auto doc_info = [&](int j, int32_t &len, int32_t &off) {
+        if (j - win >= kWave) load_window(j);
+        len = __builtin_amdgcn_readlane(wlen, j - win);
+        off = __builtin_amdgcn_readlane(woff, j - win);
+    };
+    // The next doc after j that has a tile.
+    auto next_doc = [&](int j) -> int {
+        for (;;) {
+            ++j;
+            if (j >= B) return B;
+            if (j - win >= kWave) load_window(j);
+            const unsigned long long has = __ballot(lane >= j - win && wlen > 0);
+            if (has) return win + __builtin_ctzll(has);
+            j = win + kWave - 1;  // none left in the window: continue past it
+        }
+    };
+
+    // ---- issue side: walks the range, P tiles ahead of the consume side
+    // Piece kinds: 0 whole doc (store the score), 1 head slot, 2 tail slot.
+    int i_doc = B;                 // doc of the next tile to issue (B: none left)
+    uint32_t i_t = 0, i_tend = 0;  // its tile in the doc, and the end of its piece there
+    uint32_t i_kind = 0;
+    int32_t i_len = 0;
+    uint64_t i_base = 0;
+    // Tile position of the issue side in the whole sequence: the first tile of doc i_doc
+    // is i_pos - i_t.
+    unsigned long long i_pos = r_begin;
+    auto start_doc = [&](int j, uint32_t t_begin, unsigned long long doc_first_tile) {
+        int32_t len, off;
+        doc_info(j, len, off);
+        const uint32_t nt = ((uint32_t)len + (kTileRows - 1)) / kTileRows;
+        i_doc = j;
+        i_t = t_begin;
+        i_len = len;
+        i_base = wave_uniform64((uint64_t)(uintptr_t)a.docs + (uint64_t)((int64_t)off * a.stride_bytes));
+        const unsigned long long doc_end = doc_first_tile + nt;
+        i_tend = (uint32_t)((doc_end <= r_end ? doc_end : r_end) - doc_first_tile);
+        i_kind = t_begin > 0 ? 1u : (i_tend < nt ? 2u : 0u);
+    };
+    if (r_end > r_begin) start_doc(first_doc, (uint32_t)(r_begin - first_tile), first_tile);
+
+    // Next tile of the walk into slot `slot` (a zero-size load once the range is done);
+    // returns its info word: rows | end-of-piece << 5 | kind << 6 | valid << 8 | doc << 16.
+    auto issue = [&](uint32_t slot) -> uint32_t {
+        uint32_t rows = 0, inf = 0;
+        uint64_t ub = (uint64_t)(uintptr_t)a.docs;
+        if (i_doc < B) {
+            const int left = i_len - (int)i_t * kTileRows;
+            rows = (uint32_t)(left < kTileRows ? left : kTileRows);
+            ub = wave_uniform64(i_base + (uint64_t)i_t * (uint64_t)tile_bytes);
+            const bool last = i_t + 1 == i_tend;
+            inf = rows | (last ? 1u << 5 : 0u) | (i_kind << 6) | (1u << 8) | ((uint32_t)i_doc << 16);
+            ++i_t;
+            ++i_pos;
+            if (last) {
+                // the next piece: the next doc with a tile, if the range goes on
+                if (i_pos < r_end) start_doc(next_doc(i_doc), 0, i_pos);
+                else i_doc = B;
+            }
+        }
+        rows = wave_uniform(rows);
+        const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            reinterpret_cast<void *>((uintptr_t)ub), (short)0, (int)(rows * stride_bytes), kBufferWord3);
+        // The slot's previous tile has been read (its products were issued after the
+        // reads completed); the wait makes that explicit before it is overwritten.
+        __builtin_amdgcn_s_waitcnt(kWaitAllLgkm);
+#pragma unroll
+        for (int s = 0; s < NLDD; ++s)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rsrc, (__attribute__((address_space(3))) void *)(slots + slot * TILE_CHUNKS + s * kWave), 16,
+                (int)dma_off[s], 0, 0, kDocLoadPolicy);
+        return wave_uniform(inf);
+    };
+
+    float rmax[NQT][4];
+#pragma unroll
+    for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rmax[qt][i] = NEG_INF;
+
+    auto consume = [&](uint32_t slot, uint32_t rows) {
+        // Every slot is refilled in turn, so exactly NLDD (P - 1) loads were issued after
+        // this slot's; once no more are in flight, its tile is in LDS.
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt(NLDD * (P - 1)));
+        const u32x4 *tile = slots + slot * TILE_CHUNKS;
+        u32x4 bf[NKS];
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            if constexpr (FP8D) {
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(reinterpret_cast<const char *>(tile + rd_dma[s]) + rd_half);
+                bf[s] = e4m3x8_to_16<BF16>(v[0], v[1]);
+            } else {
+                bf[s] = tile[rd_dma[s]];
+            }
+        }
+        // The accumulator of a row past the doc end starts at -inf, which keeps it out
+        // of the max; tile qt's products go into one accumulator while tile qt - 1's are
+        // folded into the running max.
+        const float c0 = row_in_tile < (int)rows ? 0.0f : NEG_INF;
+        f32x4 acc[2];
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt) {
+            f32x4 r = {c0, c0, c0, c0};
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) r = mfma16x16x32<BF16>(qf[qt][s], bf[s], r);
+            acc[qt & 1] = r;
+            if (qt > 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rmax[qt - 1][i] = __builtin_fmaxf(rmax[qt - 1][i], acc[(qt - 1) & 1][i]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) rmax[NQT - 1][i] = __builtin_fmaxf(rmax[NQT - 1][i], acc[(NQT - 1) & 1][i]);
+    };
+
+    // A piece ends: its row maxima over the 16 doc-row lanes, then the doc's score (a
+    // whole doc, summed in the score kernel's order) or the piece's slot.
+    auto finish_piece = [&](uint32_t inf) {
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rmax[qt][i] = row16_max(rmax[qt][i]);
+        const uint32_t kind = (inf >> 6) & 3u;
+        const int doc = (int)(inf >> 16);
+        if (kind == 0u) {
+            float lane_sum = 0.0f;
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                const int left = a.Lq - qt * kTileRows;
+                const int nr = left < 0 ? 0 : (left > kTileRows ? kTileRows : left);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) lane_sum += kgroup * 4 + i < nr ? rmax[qt][i] : 0.0f;
+            }
+            const int ls = __builtin_bit_cast(int, lane_sum);
+            const float s0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 0));
+            const float s1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 16));
+            const float s2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 32));
+            const float s3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(ls, 48));
+            float sum = ((s0 + s1) + s2) + s3;
+            if constexpr (FP8D) sum *= a.doc_scale;
+            if (lane == 0) a.scores[doc] = sum;
+        } else if (row_in_tile == 0) {
+            const uint32_t slot = kind == 1u ? wid : wact + wid;
+#pragma unroll
+            for (int qt = 0; qt < NQT; ++qt) {
+                f32x4 v = {rmax[qt][0], rmax[qt][1], rmax[qt][2], rmax[qt][3]};
+                *reinterpret_cast<f32x4 *>(a.partials + (size_t)slot * LQP + qt * kTileRows + kgroup * 4) = v;
+            }
+        }
+#pragma unroll
+        for (int qt = 0; qt < NQT; ++qt)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rmax[qt][i] = NEG_INF;
+    };
+
+    // The stream: slot k % P holds tile k of the walk. info[0] is the oldest slot's, the
+    // one consumed next; each step consumes it, refills its slot with the tile P ahead
+    // and shifts the queue. Tiles are issued in walk order, so once the oldest slot
+    // holds no tile, none does.
+    uint32_t info[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        info[p] = issue((uint32_t)p);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    uint32_t slot = 0;
+    while (info[0] & (1u << 8)) {
+        const uint32_t inf = info[0];
+        consume(slot, inf & 31u);
+        __builtin_amdgcn_sched_barrier(0);
+        const uint32_t fresh = issue(slot);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int p = 0; p + 1 < P; ++p) info[p] = info[p + 1];
+        info[P - 1] = fresh;
+        if (inf & (1u << 5)) finish_piece(inf);
+        slot = slot + 1u == (uint32_t)P ? 0u : slot + 1u;
+    }
+    // Every load has landed before the wave ends (the last ones were zero-size loads,
+    // which still write their LDS slot).
+    __builtin_amdgcn_s_waitcnt(kWaitAllVmem);
+}
+
+// Scores of the docs a range launch split: one wave per doc, the max over its pieces'
+// slots, then the score kernel's fixed-order sum.
+__global__ void __launch_bounds__(kScoreBlock)
+range_combine_kernel(const RangeCombineArgs a);
+
+}  // namespace maxsim

@@ -1,7 +1,9 @@
 // Score kernel instances for one query format, one doc storage and one K-step count,
 // chosen by -DMAXSIM_BF16=0|1 -DMAXSIM_FP8=0|1 -DMAXSIM_NKS=1..8 (the build compiles
 // this file once per triple, in parallel). Query tiles per group NQT run 1..8 with
-// NQT * NKS <= 32. Each file also holds the one-launch short-doc kernel of its triple.
+// NQT * NKS <= 32. Each file also holds the one-launch short-doc kernel and the
+// self-scheduling range kernel of its triple.
+#include "maxsim_range.h"
 #include "maxsim_score.h"
 #include "maxsim_short.h"
 
@@ -41,6 +43,16 @@ const void *short_entry()
     if constexpr (NQT * NKS <= maxsim::kMaxFragsPerGroup)
         return reinterpret_cast<const void *>(
             &maxsim::short_kernel<NKS, NQT, BF, FP8, pipe_depth<NQT>(), min_waves<NQT>()>);
+    else
+        return nullptr;
+}
+
+template <int NQT>
+const void *range_entry()
+{
+    if constexpr (NQT * NKS <= maxsim::kMaxFragsPerGroup)
+        return reinterpret_cast<const void *>(
+            &maxsim::range_kernel<NKS, NQT, BF, FP8, pipe_depth<NQT>(), min_waves<NQT>()>);
     else
         return nullptr;
 }
@@ -105,6 +117,31 @@ const void *MAXSIM_SHORT_LOOKUP(int nqt)
     case 6: return short_entry<6>();
     case 7: return short_entry<7>();
     case 8: return short_entry<8>();
+    default: return nullptr;
+    }
+}
+
+#if MAXSIM_BF16 && MAXSIM_FP8
+#define MAXSIM_RANGE_LOOKUP MAXSIM_CAT(maxsim_range_kernel_bf16_fp8_k, MAXSIM_NKS)
+#elif MAXSIM_BF16
+#define MAXSIM_RANGE_LOOKUP MAXSIM_CAT(maxsim_range_kernel_bf16_k, MAXSIM_NKS)
+#elif MAXSIM_FP8
+#define MAXSIM_RANGE_LOOKUP MAXSIM_CAT(maxsim_range_kernel_f16_fp8_k, MAXSIM_NKS)
+#else
+#define MAXSIM_RANGE_LOOKUP MAXSIM_CAT(maxsim_range_kernel_f16_k, MAXSIM_NKS)
+#endif
+
+const void *MAXSIM_RANGE_LOOKUP(int nqt)
+{
+    switch (nqt) {
+    case 1: return range_entry<1>();
+    case 2: return range_entry<2>();
+    case 3: return range_entry<3>();
+    case 4: return range_entry<4>();
+    case 5: return range_entry<5>();
+    case 6: return range_entry<6>();
+    case 7: return range_entry<7>();
+    case 8: return range_entry<8>();
     default: return nullptr;
     }
 }
