@@ -101,7 +101,9 @@ class MaxSimError(RuntimeError):
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "libmaxsim.so")
+    """libmaxsim.so next to this file, or the build MAXSIM_LIBRARY names (another build of
+    the same sources, e.g. one with the host code address-sanitised)."""
+    return os.environ.get("MAXSIM_LIBRARY") or os.path.join(_HERE, "libmaxsim.so")
 
 
 def load() -> ctypes.CDLL:

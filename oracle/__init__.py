@@ -180,10 +180,15 @@ class Oracle:
 
 
 def _get() -> Oracle:
+    """The oracle library: libmaxsim_oracle.so, or the build MAXSIM_ORACLE_LIBRARY names
+    (the same source built otherwise, e.g. address-sanitised)."""
     global _default
     if _default is None:
-        build(force=False)
-        _default = Oracle(LIBRARY)
+        path = os.environ.get("MAXSIM_ORACLE_LIBRARY")
+        if not path:
+            build(force=False)
+            path = LIBRARY
+        _default = Oracle(path)
     return _default
 
 
