@@ -161,6 +161,10 @@ constexpr int dma_row_chunks(int nks, bool fp8)
     return need <= 4 ? 4 : (need <= 8 ? 8 : (need <= 16 ? 16 : 32));
 }
 constexpr int dma_tile_bytes(int nks, bool fp8) { return kTileRows * dma_row_chunks(nks, fp8) * 16; }
+// 16-row MFMA row blocks per slot of the scheduled score kernel: FP8 rows are half as
+// wide, so a slot holds 32 of them (the bytes of a 16-bit tile), and every slot's fixed
+// cost (descriptor, waits, loop) is paid once per 4 KB at d = 128 in both formats.
+constexpr int score_sub(bool fp8) { return fp8 ? 2 : 1; }
 // Swizzle of slot row r: its chunk c sits at r * CP + (c ^ dma_swizzle(r, CP)). The 16
 // rows of one fragment read land in distinct 16-byte bank groups, modulo 8 and modulo
 // 16 groups, whichever the LDS serves a read in.
@@ -175,19 +179,20 @@ constexpr int dma_waves_per_simd(int nks, int nqt, bool fp8)
 // Workgroups per CU an instance is built for: what its registers allow, at most 3 (four
 // workgroups of LDS-DMA streams per CU read slower than three, measured), and fewer if
 // two tiles in flight per wave would not fit their LDS.
-constexpr int dma_blocks(int nks, int nqt, bool fp8)
+// (sub: 16-row blocks per slot; a slot holds sub * dma_tile_bytes bytes.)
+constexpr int dma_blocks(int nks, int nqt, bool fp8, int sub = 1)
 {
     int b = dma_waves_per_simd(nks, nqt, fp8) < 3 ? dma_waves_per_simd(nks, nqt, fp8) : 3;
-    while (b > 1 && kScoreWaves * 2 * dma_tile_bytes(nks, fp8) > kLdsPerCu / b - kScoreStaticLds) --b;
+    while (b > 1 && kScoreWaves * 2 * sub * dma_tile_bytes(nks, fp8) > kLdsPerCu / b - kScoreStaticLds) --b;
     return b;
 }
-// Tiles in flight per wave: up to 16 KB (8 tiles), within a workgroup's share of LDS.
-constexpr int dma_pipe(int nks, int nqt, bool fp8)
+// Slots in flight per wave: up to 16 KB (8 slots), within a workgroup's share of LDS.
+constexpr int dma_pipe(int nks, int nqt, bool fp8, int sub = 1)
 {
-    int p = 16384 / dma_tile_bytes(nks, fp8);
+    int p = 16384 / (sub * dma_tile_bytes(nks, fp8));
     if (p > 8) p = 8;
-    while (p > 1 &&
-           kScoreWaves * p * dma_tile_bytes(nks, fp8) > kLdsPerCu / dma_blocks(nks, nqt, fp8) - kScoreStaticLds)
+    while (p > 1 && kScoreWaves * p * sub * dma_tile_bytes(nks, fp8) >
+                        kLdsPerCu / dma_blocks(nks, nqt, fp8, sub) - kScoreStaticLds)
         --p;
     return p;
 }

@@ -686,7 +686,8 @@ size_t score_lds_bytes(const Config &c, int32_t d, int fmt)
     (void)d;
     const bool fp8 = (fmt & kFmtFp8Docs) != 0;
     const size_t q = q_staged(c) ? q_lds_bytes(c) : 0;
-    const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt, fp8) * dma_tile_bytes(c.nks, fp8);
+    const int sub = score_sub(fp8);
+    const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt, fp8, sub) * sub * dma_tile_bytes(c.nks, fp8);
     if (c.ngroups > 1) return q + slots;
     return q > slots ? q : slots;
 }

@@ -116,8 +116,10 @@ range_kernel(const RangeArgs a)
     int32_t *lds_len = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(S) + kRangeScanBytes);
     int32_t *lds_off = lds_len + kRangeMaxDocs;
 
-    // ---- prologue: lengths and offsets (4 docs per thread, one round of loads with the
-    // query tile's), tile counts and S
+    // ---- prologue: lengths and offsets (4 docs per thread) and the query tile, all in
+    // one round of loads. The schedule (tile counts, S, each wave's first doc) needs only
+    // the lengths and offsets, so it is formed while the query is still arriving; the
+    // query is written to LDS afterwards (its region is apart from S's).
     int32_t len4[4], off4[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -125,15 +127,17 @@ range_kernel(const RangeArgs a)
         len4[j] = i < B ? a.lengths[i] : 0;
         off4[j] = i < B ? a.offsets[i] : 0;
     }
-    {
-        constexpr int CPR = DPAD / 8;
-        for (int e = threadIdx.x; e < LQP * CPR; e += kScoreBlock) {
-            const int r = e / CPR;
-            const int c = e - r * CPR;
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (r < a.Lq && c * 8 < a.d) v = *reinterpret_cast<const u32x4 *>(a.Q + (size_t)r * a.d + c * 8);
-            *reinterpret_cast<u32x4 *>(qs + r * LDQ + c * 8) = v;
-        }
+    constexpr int CPR = DPAD / 8;                                        // 16-byte chunks per query row
+    constexpr int QL = (LQP * CPR + kScoreBlock - 1) / kScoreBlock;     // query chunks per thread
+    u32x4 qv[QL];
+#pragma unroll
+    for (int k = 0; k < QL; ++k) {
+        const int e = (int)threadIdx.x + k * kScoreBlock;
+        const int r = e / CPR;
+        const int c = e - r * CPR;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (e < LQP * CPR && r < a.Lq && c * 8 < a.d) v = *reinterpret_cast<const u32x4 *>(a.Q + (size_t)r * a.d + c * 8);
+        qv[k] = v;
     }
     uint32_t nt4[4];
     unsigned long long mine = 0;
@@ -218,6 +222,15 @@ range_kernel(const RangeArgs a)
         wlen = lds_len[first_doc + lane];
         woff = lds_off[first_doc + lane];
     }
+    // Now the query tile, zero-padded, into LDS; then every wave's fragments from it.
+#pragma unroll
+    for (int k = 0; k < QL; ++k) {
+        const int e = (int)threadIdx.x + k * kScoreBlock;
+        const int r = e / CPR;
+        const int c = e - r * CPR;
+        if (e < LQP * CPR) *reinterpret_cast<u32x4 *>(qs + r * LDQ + c * 8) = qv[k];
+    }
+    __syncthreads();
 
     u32x4 qf[NQT][NKS];
 #pragma unroll

@@ -167,10 +167,13 @@ __global__ void __launch_bounds__(kScoreBlock, MINW)
 score_kernel(const ScoreArgs a)
 {
     constexpr int DPAD = NKS * kStepK;
-    // Doc tiles are loaded with LDS-DMA straight into the wave's P tile slots.
+    // Doc rows are loaded with LDS-DMA straight into the wave's P slots. A slot holds SUB
+    // 16-row MFMA blocks: 16 rows of 16-bit docs, 32 of FP8 docs (the same bytes).
+    constexpr int SUB = score_sub(FP8D);
+    constexpr int SROWS = SUB * kTileRows;         // doc rows per slot
     constexpr int CP = dma_row_chunks(NKS, FP8D);  // slot row: 16-byte chunks
-    constexpr int NLDD = CP / 4;                   // LDS-DMA loads per tile, 64 chunks each
-    constexpr int TILE_CHUNKS = kTileRows * CP;
+    constexpr int TILE_CHUNKS = SROWS * CP;        // 16-byte chunks per slot
+    constexpr int NLDD = TILE_CHUNKS / kWave;      // LDS-DMA loads per slot, 64 chunks each
     constexpr int LDQ = DPAD + 8;  // LDS row pitch (halves): 16 B skew against bank conflicts
     constexpr float NEG_INF = -__builtin_huge_valf();
 
@@ -210,7 +213,7 @@ score_kernel(const ScoreArgs a)
 
     // ---- per-lane load and staging geometry
     const uint32_t stride_bytes = (uint32_t)a.stride_bytes;
-    const uint32_t tile_bytes = (uint32_t)kTileRows * stride_bytes;  // bytes between tiles of a doc
+    const uint32_t tile_bytes = (uint32_t)SROWS * stride_bytes;  // bytes between slots of a doc
     const int row_in_tile = lane & 15;
     const int kgroup = lane >> 4;
     const int C = FP8D ? a.d / 16 : a.d / 8;  // 16-byte chunks per doc row
@@ -232,16 +235,19 @@ score_kernel(const ScoreArgs a)
         const int q = s * kWave + lane;
         const int row = q / CP;
         const int c = (q % CP) ^ dma_swizzle(row, CP);
-        dma_off[s] = c < C ? (uint32_t)row * stride_bytes + (uint32_t)c * 16u : (uint32_t)kTileRows * stride_bytes;
+        dma_off[s] = c < C ? (uint32_t)row * stride_bytes + (uint32_t)c * 16u : (uint32_t)SROWS * stride_bytes;
     }
-    // B fragment of K-step s, row row_in_tile: 16-bit docs, chunk kgroup + 4 s (8
-    // columns); FP8 docs, the 8 bytes at half kgroup % 2 of chunk kgroup / 2 + 2 s.
-    int rd_dma[NKS];
+    // B fragment of K-step s, row row_in_tile of block h: 16-bit docs, chunk kgroup + 4 s
+    // (8 columns); FP8 docs, the 8 bytes at half kgroup % 2 of chunk kgroup / 2 + 2 s.
+    int rd_dma[SUB][NKS];
 #pragma unroll
-    for (int s = 0; s < NKS; ++s) {
-        const int c = FP8D ? (kgroup >> 1) + 2 * s : kgroup + 4 * s;
-        rd_dma[s] = row_in_tile * CP + (c ^ dma_swizzle(row_in_tile, CP));
-    }
+    for (int h = 0; h < SUB; ++h)
+#pragma unroll
+        for (int s = 0; s < NKS; ++s) {
+            const int c = FP8D ? (kgroup >> 1) + 2 * s : kgroup + 4 * s;
+            const int row = h * kTileRows + row_in_tile;
+            rd_dma[h][s] = row * CP + (c ^ dma_swizzle(row, CP));
+        }
     const int rd_half = (kgroup & 1) * 8;  // FP8 docs: byte offset in the chunk
 
     // Query fragments of register group grp: from LDS when the query tiles are staged
@@ -358,15 +364,16 @@ score_kernel(const ScoreArgs a)
         return sp;
     };
 
-    // Loads of tile t of span sp into pipeline slot `slot`. The descriptor covers only
-    // the tile's valid rows (none for t past the span, or for an invalid span).
+    // Loads of slot-tile t (rows [t SROWS, (t + 1) SROWS) of a span) into pipeline slot
+    // `slot`. The descriptor covers only the valid rows (none for t past the span, or
+    // for an invalid span).
     auto issue = [&](int slot, uint64_t base, int nrows, int t) {
-        // Valid rows of the tile, clamped in two steps on scalar registers (one clamp
-        // would become a vector med3, a vector multiply and a readfirstlane).
-        const int left = (int)wave_uniform((uint32_t)(nrows - t * kTileRows));
+        // Valid rows, clamped in two steps on scalar registers (one clamp would become a
+        // vector med3, a vector multiply and a readfirstlane).
+        const int left = (int)wave_uniform((uint32_t)(nrows - t * SROWS));
         const int lo = (int)wave_uniform((uint32_t)(left > 0 ? left : 0));
-        const uint32_t rows = (uint32_t)(lo < kTileRows ? lo : kTileRows);
-        // t < 2^27 and a tile is at most 16 rows of 2^25 bytes: a 32 x 32 -> 64-bit product.
+        const uint32_t rows = (uint32_t)(lo < SROWS ? lo : SROWS);
+        // t < 2^27 and a slot is at most 32 rows of 2^24 bytes: a 32 x 32 -> 64-bit product.
         const uint64_t ub = wave_uniform64(base + (uint64_t)(uint32_t)t * (uint64_t)tile_bytes);
         const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
             reinterpret_cast<void *>((uintptr_t)ub), (short)0, (int)(rows * stride_bytes), kBufferWord3);
@@ -381,44 +388,50 @@ score_kernel(const ScoreArgs a)
     };
 
     float rmax[NQT][4];
-    // Tile t (in slot `slot`) of a span with `nrows` rows: stage, multiply, max.
+    // Slot-tile t (in slot `slot`) of a span with `nrows` rows: stage, multiply, max, one
+    // 16-row block at a time (a block past the span's rows is skipped, except the first).
     auto consume = [&](int slot, int nrows, int t) {
-        const int left = nrows - t * kTileRows;
-        u32x4 bf[NKS];
         // Every slot is refilled in turn, so exactly NLDD (P - 1) loads were issued after
-        // this slot's; once no more are in flight, its tile is in LDS.
+        // this slot's; once no more are in flight, its rows are in LDS.
         __builtin_amdgcn_s_waitcnt(wait_vmcnt(NLDD * (P - 1)));
 #pragma unroll
-        for (int s = 0; s < NKS; ++s) {
-            if constexpr (FP8D) {
-                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                const u32x2 v = *reinterpret_cast<const u32x2 *>(
-                    reinterpret_cast<const char *>(slots + slot * TILE_CHUNKS + rd_dma[s]) + rd_half);
-                bf[s] = e4m3x8_to_16<BF16>(v[0], v[1]);
-            } else {
-                bf[s] = slots[slot * TILE_CHUNKS + rd_dma[s]];
+        for (int h = 0; h < SUB; ++h) {
+            const int left = (int)wave_uniform((uint32_t)(nrows - (t * SUB + h) * kTileRows));
+            if (h > 0 && left <= 0) break;
+            u32x4 bf[NKS];
+#pragma unroll
+            for (int s = 0; s < NKS; ++s) {
+                if constexpr (FP8D) {
+                    typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                    const u32x2 v = *reinterpret_cast<const u32x2 *>(
+                        reinterpret_cast<const char *>(slots + slot * TILE_CHUNKS + rd_dma[h][s]) + rd_half);
+                    bf[s] = e4m3x8_to_16<BF16>(v[0], v[1]);
+                } else {
+                    bf[s] = slots[slot * TILE_CHUNKS + rd_dma[h][s]];
+                }
             }
-        }
-        // The accumulator starts at 0 for this lane's doc row if the row is valid and
-        // at -inf if not (past the doc end): -inf + a finite dot stays -inf, so invalid
-        // rows never win the max and need no masking.
-        const float c0 = row_in_tile < left ? 0.0f : NEG_INF;
-        // Query tile qt's products go into one accumulator while tile qt - 1's, in the
-        // other, are folded into the running max: the max waits on finished MFMAs.
-        f32x4 acc[2];
+            // The accumulator starts at 0 for this lane's doc row if the row is valid and
+            // at -inf if not (past the doc end): -inf + a finite dot stays -inf, so invalid
+            // rows never win the max and need no masking.
+            const float c0 = row_in_tile < left ? 0.0f : NEG_INF;
+            // Query tile qt's products go into one accumulator while tile qt - 1's, in the
+            // other, are folded into the running max: the max waits on finished MFMAs.
+            f32x4 acc[2];
 #pragma unroll
-        for (int qt = 0; qt < NQT; ++qt) {
-            f32x4 a = {c0, c0, c0, c0};
+            for (int qt = 0; qt < NQT; ++qt) {
+                f32x4 a = {c0, c0, c0, c0};
 #pragma unroll
-            for (int s = 0; s < NKS; ++s) a = mfma16x16x32<BF16>(qf[qt][s], bf[s], a);
-            acc[qt & 1] = a;
-            if (qt > 0) {
+                for (int s = 0; s < NKS; ++s) a = mfma16x16x32<BF16>(qf[qt][s], bf[s], a);
+                acc[qt & 1] = a;
+                if (qt > 0) {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) rmax[qt - 1][i] = __builtin_fmaxf(rmax[qt - 1][i], acc[(qt - 1) & 1][i]);
+                    for (int i = 0; i < 4; ++i)
+                        rmax[qt - 1][i] = __builtin_fmaxf(rmax[qt - 1][i], acc[(qt - 1) & 1][i]);
+                }
             }
-        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) rmax[NQT - 1][i] = __builtin_fmaxf(rmax[NQT - 1][i], acc[(NQT - 1) & 1][i]);
+            for (int i = 0; i < 4; ++i) rmax[NQT - 1][i] = __builtin_fmaxf(rmax[NQT - 1][i], acc[(NQT - 1) & 1][i]);
+        }
     };
 
     // Descriptor queue: cur and nxt resolved, the one after that in flight.
@@ -470,9 +483,10 @@ score_kernel(const ScoreArgs a)
         const bool more_groups = grp + 1 < ngroups;
         const uint64_t c_base = wave_uniform64(cur.base);
         const int c_rows = (int)wave_uniform((uint32_t)cur.nrows);
-        // An empty doc runs as one tile with no valid rows (zero-size loads, all
+        // An empty doc runs as one slot with no valid rows (zero-size loads, all
         // accumulators -inf): its maxima stay -inf, and the loop shape never changes.
-        const int c_tiles = (int)wave_uniform((uint32_t)(cur.ntiles > 0 ? cur.ntiles : 1));
+        // The span's 16-row tiles fill ceil(ntiles / SUB) slots.
+        const int c_tiles = (int)wave_uniform((uint32_t)(cur.ntiles > 0 ? (cur.ntiles + SUB - 1) / SUB : 1));
         const uint64_t n_base = wave_uniform64(more_groups ? cur.base : nxt.base);
         const int n_rows = (int)wave_uniform((uint32_t)(more_groups ? cur.nrows : nxt.nrows));
 

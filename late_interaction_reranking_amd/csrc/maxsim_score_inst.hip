@@ -25,16 +25,18 @@ constexpr bool FP8 = MAXSIM_FP8 != 0;
 // Pipeline depth in doc tiles and occupancy target (workgroups of 4 waves per CU,
 // i.e. waves per SIMD) for the register allocation: the LDS-DMA rule shared with the
 // host (maxsim::dma_pipe, maxsim::dma_blocks).
-template <int NQT>
+// (sub: 16-row blocks per slot; the scheduled score kernel's FP8 slots hold 32 rows,
+// the one-launch kernels' 16.)
+template <int NQT, int SUB = 1>
 constexpr int pipe_depth()
 {
-    return maxsim::dma_pipe(NKS, NQT, FP8);
+    return maxsim::dma_pipe(NKS, NQT, FP8, SUB);
 }
 
-template <int NQT>
+template <int NQT, int SUB = 1>
 constexpr int min_waves()
 {
-    return maxsim::dma_blocks(NKS, NQT, FP8);
+    return maxsim::dma_blocks(NKS, NQT, FP8, SUB);
 }
 
 template <int NQT>
@@ -62,7 +64,8 @@ const void *entry()
 {
     if constexpr (NQT * NKS <= maxsim::kMaxFragsPerGroup)
         return reinterpret_cast<const void *>(
-            &maxsim::score_kernel<NKS, NQT, BF, FP8, pipe_depth<NQT>(), min_waves<NQT>()>);
+            &maxsim::score_kernel<NKS, NQT, BF, FP8, pipe_depth<NQT, maxsim::score_sub(FP8)>(),
+                                  min_waves<NQT, maxsim::score_sub(FP8)>()>);
     else
         return nullptr;
 }
