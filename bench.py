@@ -423,7 +423,7 @@ def main() -> int:
                     help="single-query workloads: 'staged' times maxsim_plan, maxsim_score and "
                          "maxsim_finish on a caller workspace (events around the score kernel); "
                          "'one-shot' times maxsim_rerank (maxsim_rerank_fp8) itself, events around the "
-                         "whole call: for at most 1024 docs the self-scheduling range kernel and its "
+                         "whole call: for at most 8192 docs the self-scheduling range kernel and its "
                          "combine, else plan, score and combine")
     ap.add_argument("--graph", action="store_true",
                     help="time the steps as replays of one step captured in a HIP graph (no host "
@@ -708,7 +708,7 @@ def main() -> int:
         "launch": ("HIP graph replay of one captured step" if args.graph
                    else "eager: one host launch per kernel"),
         "path": ("one launch, one workgroup per doc (maxsim_rerank_short)" if args.short
-                 else (("one-shot maxsim_rerank: self-scheduling range kernel + combine" if w.B <= 1024
+                 else (("one-shot maxsim_rerank: self-scheduling range kernel + combine" if w.B <= 8192
                         else "one-shot maxsim_rerank: plan, score, combine") if one_shot_path
                        else "scheduled: plan, score, combine")),
         "ms_per_step_eager": ms_per_step_eager,

@@ -88,6 +88,10 @@ extern "C" {
  * MaxSim scores, fp16 Q and docs (IEEE binary16).
  * Uses the stream's one-shot workspace (conventions above), so concurrent calls on
  * different streams do not interfere; calls from several host threads are safe.
+ * Launches: for 1 <= B <= 8192 with ceil(Lq / 16) <= 8 and ceil(Lq / 16) * ceil(d / 32)
+ * <= 32 (the query held in registers at once), a self-scheduling kernel that cuts the docs' 16-row tiles into equal contiguous ranges
+ * per wave, then a combine launch for the docs it split; otherwise the staged plan,
+ * score and finish below. Both give bitwise the same scores.
  */
 MAXSIM_API int maxsim_rerank(const void *Q, int32_t Lq, int32_t d,
                   const void *docs, int64_t stride,

@@ -512,7 +512,7 @@ range_combine_kernel(const RangeCombineArgs a)
         typedef __attribute__((address_space(4))) const unsigned long long ConstU64;
         const unsigned long long s = ((ConstU64 *)a.scan)[di];
         const unsigned long long e = ((ConstU64 *)a.scan)[di + 1];
-        if (e == s) continue;
+        if (e <= s || e > T) continue;  // no tile (e > T: not a scan the range kernel wrote)
         const uint32_t w_lo = range_wave(s, T, wact);
         const uint32_t w_hi = range_wave(e - 1ull, T, wact);
         if (w_lo == w_hi) continue;
@@ -1016,7 +1016,7 @@ int score_launch_waves(int fmt, int32_t Lq, int32_t d, uint32_t *waves)
 
 // ---------------------------------------------------------------- range launches
 //
-// A single-query batch of at most kRangeMaxDocs docs whose query fits one register group
+// A single-query batch of at most kRangeMaxDocs (8192) docs whose query fits one register group
 // runs as two launches: the self-scheduling range kernel (csrc/maxsim_range.h), which
 // cuts the docs' tiles into equal contiguous ranges per wave, and range_combine_kernel
 // for the docs it split. No plan launch. Its workspace holds the tile prefix sums (the
@@ -1038,16 +1038,31 @@ const void *range_fn(int fmt, const Config &c)
     }
 }
 
-// Dynamic LDS: the query tile and, after it, the prologue's prefix sums; then the same
-// tile slots as the score kernel, over both.
-size_t range_scan_lds(const Config &c) { return (q_lds_bytes(c) + 15) & ~size_t(15); }
+// Dynamic LDS: the query tile, then (in the prologue) the doc lengths, 1024 per 4-doc
+// chunk a thread takes, and the doc offsets in 256-doc pieces where they fit without
+// growing the allocation (always for at most 1024 docs: 4 KB); then the same tile slots
+// as the score kernel over all of it.
+struct RangeLds {
+    size_t len, off, bytes;  // byte offsets of the lengths and offsets (off 0: not in LDS); size
+};
 
-size_t range_lds_bytes(const Config &c, int fmt)
+RangeLds range_lds(const Config &c, int fmt, int32_t B)
 {
     const bool fp8 = (fmt & kFmtFp8Docs) != 0;
-    const size_t q = range_scan_lds(c) + kRangePrologueBytes;
+    RangeLds r;
+    r.len = (q_lds_bytes(c) + 15) & ~size_t(15);
+    const size_t nch = ((size_t)B + kRangeDocsPerChunkRow - 1) / kRangeDocsPerChunkRow;
+    const size_t pro = r.len + 4 * kRangeDocsPerChunkRow * nch;
+    const size_t off_bytes = (size_t)4 * 4 * kWave * (((size_t)B + 4 * kWave - 1) / (4 * kWave));
     const size_t slots = (size_t)kScoreWaves * dma_pipe(c.nks, c.nqt, fp8) * dma_tile_bytes(c.nks, fp8);
-    return q > slots ? q : slots;
+    const size_t base = pro > slots ? pro : slots;
+    r.off = 0;
+    r.bytes = base;
+    if (pro + off_bytes <= base || B <= kRangeDocsPerChunkRow) {
+        r.off = pro;
+        r.bytes = pro + off_bytes > base ? pro + off_bytes : base;
+    }
+    return r;
 }
 
 struct RangePlan {
@@ -1063,7 +1078,7 @@ int range_plan(int fmt, int32_t Lq, int32_t d, int32_t B, RangePlan *rp)
     if (c.ngroups != 1 || c.nqt * c.nks > kMaxFragsPerGroup) return MAXSIM_ERR_UNSUPPORTED;
     rp->fn = range_fn(fmt, c);
     if (!rp->fn) return MAXSIM_ERR_UNSUPPORTED;
-    rp->lds = range_lds_bytes(c, fmt);
+    rp->lds = range_lds(c, fmt, B).bytes;
     int per_cu = 0;
     if (score_blocks_per_cu(rp->fn, rp->lds, &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     DeviceFacts f;
@@ -1094,7 +1109,9 @@ int enqueue_range(int fmt, const RangePlan &rp, const void *Q, int32_t Lq, int32
     a.B = B;
     a.d = d;
     a.Lq = Lq;
-    a.scan_lds = (uint32_t)range_scan_lds(c);
+    const RangeLds rl = range_lds(c, fmt, B);
+    a.len_lds = (uint32_t)rl.len;
+    a.off_lds = (uint32_t)rl.off;
     a.doc_scale = fp8 ? doc_scale : 1.0f;
     void *args[] = {&a};
     if (hipLaunchKernel(rp.fn, dim3(rp.blocks), dim3(kScoreBlock), args, rp.lds, stream) != hipSuccess)

@@ -1,4 +1,4 @@
-// MaxSim score kernel for small single-query batches (at most kRangeMaxDocs docs, one
+// MaxSim score kernel for single-query batches of at most kRangeMaxDocs docs (one
 // register group of query tiles) that schedules itself: one launch, no plan launch.
 //
 // Operation (Flash-MaxSim rerank page, docs.vllm.ai,
@@ -10,9 +10,12 @@
 // tiles: doc i holds tiles [S_i, S_i + nt_i), nt_i = ceil(len_i / 16), S the exclusive
 // prefix sums. It is cut into W_act ranges of equal size (to one tile): wave w takes
 // tiles [floor(w T / W_act), floor((w + 1) T / W_act)), W_act = min(W, T / kMinRangeTiles)
-// (at least 1). Every workgroup loads the lengths and forms S in LDS itself, so nothing
-// runs before this launch, and the balance is exact: with a few tiles per wave, a deal
-// of whole docs or of chunks leaves the slowest wave about twice the average.
+// (at least 1). Every workgroup loads the lengths and forms the cut itself: each thread
+// sums the tiles of a contiguous block of up to 32 docs, a block-wide scan gives each
+// block's first tile, and each wave finds the block holding its first tile (a count over
+// the 256 block starts) and the doc within it (a scan over the block's docs).
+// So nothing runs before this launch, and the balance is exact: with a few tiles per
+// wave, a deal of whole docs or of chunks leaves the slowest wave about twice the average.
 //
 // Pieces. A wave's range holds whole docs and, at its two ends, pieces of docs that
 // other waves also cover. A whole doc is summed and stored here, as the score kernel
@@ -29,22 +32,22 @@
 // docs P tiles ahead of the consume side and leaves, per slot, what the consume side
 // needs: the tile's valid rows, whether it ends a piece, and the piece's doc and slot.
 // Doc boundaries therefore cost no pipeline bubble. The doc lengths and offsets come
-// from a window of 64 docs held one per lane; only the prologue needs S, which it keeps
-// in the LDS that the tile slots take over afterwards. Tile positions are 64-bit: docs
-// may overlap, so T is bounded only by B * 2^27.
+// from a window of 64 docs held one per lane (the first filled by the prologue, later
+// ones loaded). Tile positions are 64-bit: docs may overlap, so T is bounded only by
+// B * 2^27.
 #pragma once
+
+#include <type_traits>
 
 #include "maxsim_score.h"
 
 namespace maxsim {
 
-constexpr int kRangeMaxDocs = 1024;           // docs of a range launch: 4 per thread
-constexpr uint32_t kMinRangeTiles = 2;        // fewest tiles per active wave
-// LDS of the prologue, after the query tile: S (64-bit, B + 1 entries), then the lengths
-// and offsets (32-bit, B each). The tile slots take it over once the waves have their
-// first docs.
-constexpr size_t kRangeScanBytes = 8 * (kRangeMaxDocs + 2);
-constexpr size_t kRangePrologueBytes = kRangeScanBytes + 8 * kRangeMaxDocs;
+constexpr int kRangeChunksPerThread = 8;                            // most 4-doc chunks a prologue thread sums
+constexpr int kRangeMaxBlockDocs = 4 * kRangeChunksPerThread;       // most docs in a thread's block: 32
+constexpr int kRangeDocsPerChunkRow = 4 * kScoreBlock;              // docs covered per chunk a thread takes
+constexpr int kRangeMaxDocs = kRangeMaxBlockDocs * kScoreBlock;     // docs of a range launch: 8192
+constexpr uint32_t kMinRangeTiles = 2;                           // fewest tiles per active wave
 
 struct RangeArgs {
     const uint16_t *Q;             // [Lq, d]
@@ -56,7 +59,8 @@ struct RangeArgs {
     unsigned long long *scan;      // workspace: S_0 .. S_B (S_B = T) for the combine kernel
     float *partials;               // workspace: [2 W][16 NQT] head slots, then tail slots
     int32_t B, d, Lq;
-    uint32_t scan_lds;             // byte offset of S in the dynamic LDS (after the query tile)
+    uint32_t len_lds;              // byte offset of the prologue's doc lengths in the dynamic LDS
+    uint32_t off_lds;              // and of its doc offsets (0: the offsets stay in global memory)
     float doc_scale;               // FP8 docs: multiplies each sum (unused otherwise)
 };
 
@@ -89,6 +93,29 @@ __host__ __device__ inline uint32_t range_active_waves(unsigned long long T, uin
     return w < waves ? (uint32_t)w : waves;
 }
 
+// Lane l of a DPP move with control C into rows R (others 0; lanes with no source 0).
+template <int C, int R>
+__device__ __forceinline__ unsigned long long dpp_move64(unsigned long long v)
+{
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, C, R, 0xf, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), C, R, 0xf, true);
+    return ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+// Inclusive prefix sum over the wave's 64 lanes, on the VALU: shifts by 1, 2, 4 and 8
+// lanes within each row of 16, then lane 15 of each row added into the row after it (rows
+// 1 and 3) and lane 31 into rows 2 and 3.
+__device__ __forceinline__ unsigned long long wave_scan_incl64(unsigned long long x)
+{
+    x += dpp_move64<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_move64<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_move64<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_move64<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_move64<0x142, 0xa>(x);  // row_bcast:15
+    x += dpp_move64<0x143, 0xc>(x);  // row_bcast:31
+    return x;
+}
+
 template <int NKS, int NQT, bool BF16, bool FP8D, int P, int MINW>
 __global__ void __launch_bounds__(kScoreBlock, MINW)
 range_kernel(const RangeArgs a)
@@ -101,8 +128,9 @@ range_kernel(const RangeArgs a)
     constexpr int LQP = NQT * kTileRows;          // padded query rows
     constexpr float NEG_INF = -__builtin_huge_valf();
 
-    extern __shared__ __attribute__((aligned(16))) uint16_t qs[];  // Q tile | S; then the tile slots
-    __shared__ unsigned long long wave_tiles[kScoreWaves];
+    extern __shared__ __attribute__((aligned(16))) uint16_t qs[];  // Q tile | lengths | offsets; then the tile slots
+    __shared__ unsigned long long wave_tiles[kScoreWaves];          // tiles of each wave's docs
+    __shared__ unsigned long long blk_first[kScoreBlock];           // first tile of each thread's block
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = (int)wave_uniform(threadIdx.x / kWave);
@@ -111,21 +139,29 @@ range_kernel(const RangeArgs a)
     const uint32_t W = gridDim.x * kScoreWaves;
     const uint32_t wid = blockIdx.x * kScoreWaves + wave;
     const int B = a.B;
-    unsigned long long *S = reinterpret_cast<unsigned long long *>(reinterpret_cast<char *>(qs) + a.scan_lds);
 
-    int32_t *lds_len = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(S) + kRangeScanBytes);
-    int32_t *lds_off = lds_len + kRangeMaxDocs;
-
-    // ---- prologue: lengths and offsets (4 docs per thread) and the query tile, all in
-    // one round of loads. The schedule (tile counts, S, each wave's first doc) needs only
-    // the lengths and offsets, so it is formed while the query is still arriving; the
-    // query is written to LDS afterwards (its region is apart from S's).
-    int32_t len4[4], off4[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int i = 4 * (int)threadIdx.x + j;
-        len4[j] = i < B ? a.lengths[i] : 0;
-        off4[j] = i < B ? a.offsets[i] : 0;
+    // ---- prologue: one round of loads. The lengths (and, when the LDS has room, the
+    // offsets) go to LDS by DMA, 256 docs per wave instruction; the query's chunks go to
+    // registers and from there to LDS.
+    const int nch = (B + kRangeDocsPerChunkRow - 1) / kRangeDocsPerChunkRow;  // 4-doc chunks per thread
+    const int dpt = 4 * nch;                                                  // docs per thread block
+    int32_t *lds_len = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(qs) + a.len_lds);
+    int32_t *lds_off = reinterpret_cast<int32_t *>(reinterpret_cast<char *>(qs) + a.off_lds);
+    {
+        const int pieces = (B + 4 * kWave - 1) / (4 * kWave);
+        const __amdgpu_buffer_rsrc_t rlen = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t *>(a.lengths), (short)0, B * 4, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t roff = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<int32_t *>(a.offsets), (short)0, B * 4, kBufferWord3);
+        for (int p = wave; p < pieces; p += kScoreWaves) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rlen, (__attribute__((address_space(3))) void *)(lds_len + p * 4 * kWave), 16,
+                p * 16 * kWave + lane * 16, 0, 0, 0);
+            if (a.off_lds)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    roff, (__attribute__((address_space(3))) void *)(lds_off + p * 4 * kWave), 16,
+                    p * 16 * kWave + lane * 16, 0, 0, 0);
+        }
     }
     constexpr int CPR = DPAD / 8;                                        // 16-byte chunks per query row
     constexpr int QL = (LQP * CPR + kScoreBlock - 1) / kScoreBlock;     // query chunks per thread
@@ -139,90 +175,7 @@ range_kernel(const RangeArgs a)
         if (e < LQP * CPR && r < a.Lq && c * 8 < a.d) v = *reinterpret_cast<const u32x4 *>(a.Q + (size_t)r * a.d + c * 8);
         qv[k] = v;
     }
-    uint32_t nt4[4];
-    unsigned long long mine = 0;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        nt4[j] = len4[j] > 0 ? ((uint32_t)len4[j] + (kTileRows - 1)) / kTileRows : 0u;
-        mine += nt4[j];
-    }
-    // inclusive scan of the per-thread totals across the wave, then across the waves
-    unsigned long long incl = mine;
-#pragma unroll
-    for (int o = 1; o < kWave; o <<= 1) {
-        const unsigned long long up = __shfl_up(incl, o);
-        if (lane >= o) incl += up;
-    }
-    if (lane == kWave - 1) wave_tiles[wave] = incl;
-    __syncthreads();
-    unsigned long long before = incl - mine, T = 0;
-#pragma unroll
-    for (int v = 0; v < kScoreWaves; ++v) {
-        const unsigned long long t = wave_tiles[v];
-        if (v < wave) before += t;
-        T += t;
-    }
-    {
-        unsigned long long s = before;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = 4 * (int)threadIdx.x + j;
-            if (i < B) {
-                S[i] = s;
-                lds_len[i] = len4[j];
-                lds_off[i] = off4[j];
-            }
-            s += nt4[j];
-        }
-        if (threadIdx.x == 0) S[B] = T;
-    }
-    if (blockIdx.x == 0) {
-        // For the combine kernel: S, with S_B = T; and -inf for empty docs (no tile, so
-        // no piece and no combine).
-        unsigned long long s = before;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int i = 4 * (int)threadIdx.x + j;
-            if (i < B) {
-                a.scan[i] = s;
-                if (nt4[j] == 0u) a.scores[i] = NEG_INF;
-            }
-            s += nt4[j];
-        }
-        if (threadIdx.x == 0) a.scan[B] = T;
-    }
-    __syncthreads();
-
-    // ---- this wave's range and its first doc (largest i with S_i <= first tile)
-    const uint32_t wact = range_active_waves(T, W);
-    unsigned long long r_begin = 0, r_end = 0;
-    if (wid < wact) {
-        r_begin = range_start(wid, T, wact);
-        r_end = wid + 1 == wact ? T : range_start(wid + 1, T, wact);
-    }
-    int first_doc = 0;
-    unsigned long long first_tile = 0;  // S of first_doc
-    if (r_end > r_begin) {
-        int lo = 0, hi = B;  // S[lo] <= r_begin < S[hi]
-        while (hi - lo > 1) {
-            const int mid = (lo + hi) >> 1;
-            if (S[mid] <= r_begin) lo = mid;
-            else hi = mid;
-        }
-        first_doc = lo;
-        first_tile = S[lo];
-    }
-    first_doc = (int)wave_uniform((uint32_t)first_doc);
-    first_tile = wave_uniform64(first_tile);
-    r_begin = wave_uniform64(r_begin);
-    r_end = wave_uniform64(r_end);
-    // The first window of doc lengths and offsets (doc first_doc + l in lane l), from LDS.
-    int32_t wlen = 0, woff = 0;
-    if (first_doc + lane < B) {
-        wlen = lds_len[first_doc + lane];
-        woff = lds_off[first_doc + lane];
-    }
-    // Now the query tile, zero-padded, into LDS; then every wave's fragments from it.
+    __builtin_amdgcn_s_waitcnt(kWaitAllVmem);
 #pragma unroll
     for (int k = 0; k < QL; ++k) {
         const int e = (int)threadIdx.x + k * kScoreBlock;
@@ -232,12 +185,113 @@ range_kernel(const RangeArgs a)
     }
     __syncthreads();
 
+    // ---- the schedule. Thread t's block of docs is [t dpt, (t + 1) dpt); its tiles are
+    // summed chunk by chunk, starting at chunk t mod nch (the threads of a wave then read
+    // distinct banks); a block-wide scan gives each block's first tile.
+    auto tiles_of_len = [](int32_t len) -> uint32_t {
+        return len > 0 ? ((uint32_t)len + (kTileRows - 1)) / kTileRows : 0u;
+    };
+    // N chunk reads (N >= nch) issued together; a read past the thread's nch chunks
+    // repeats one and is not counted.
+    auto block_tiles = [&](auto n) -> unsigned long long {
+        constexpr int N = decltype(n)::value;
+        const int t = (int)threadIdx.x;
+        int c = t % nch;
+        int4 v[N];
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            v[j] = *reinterpret_cast<const int4 *>(lds_len + t * dpt + 4 * c);
+            c = c + 1 == nch ? 0 : c + 1;
+        }
+        unsigned long long sum = 0;
+        c = t % nch;
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+            const int i0 = t * dpt + 4 * c;
+            uint32_t nt = tiles_of_len(i0 < B ? v[j].x : 0) + tiles_of_len(i0 + 1 < B ? v[j].y : 0);
+            unsigned long long pair = (unsigned long long)nt +
+                                      tiles_of_len(i0 + 2 < B ? v[j].z : 0) + tiles_of_len(i0 + 3 < B ? v[j].w : 0);
+            sum += j < nch ? pair : 0ull;
+            c = c + 1 == nch ? 0 : c + 1;
+        }
+        return sum;
+    };
+    const unsigned long long mine = nch <= 2 ? block_tiles(std::integral_constant<int, 2>{})
+                                             : block_tiles(std::integral_constant<int, kRangeChunksPerThread>{});
+    const unsigned long long incl = wave_scan_incl64(mine);
+    if (lane == kWave - 1) wave_tiles[wave] = incl;
+    __syncthreads();
+    unsigned long long before = incl - mine, T = 0;  // first tile of this thread's block; all tiles
+#pragma unroll
+    for (int v = 0; v < kScoreWaves; ++v) {
+        const unsigned long long t = wave_tiles[v];
+        if (v < wave) before += t;
+        T += t;
+    }
+    blk_first[threadIdx.x] = before;
+    __syncthreads();
+
+    // Lane l of block k: doc k dpt + l's length (0 past the block or the batch), tiles and
+    // first tile.
+    auto block_len = [&](int k) -> int32_t {
+        const int i = k * dpt + lane;
+        return lane < dpt && i < B ? lds_len[i] : 0;
+    };
+    auto block_first = [&](int k, uint32_t nt) -> unsigned long long {
+        return blk_first[k] + wave_scan_incl64(nt) - nt;
+    };
+
+    // ---- this wave's range and its first doc: the block holding the range's first
+    // tile (the last block whose first tile is at most it), then the doc within it.
+    const uint32_t wact = range_active_waves(T, W);
+    unsigned long long r_begin = 0, r_end = 0;
+    if (wid < wact) {
+        r_begin = range_start(wid, T, wact);
+        r_end = wid + 1 == wact ? T : range_start(wid + 1, T, wact);
+    }
+    r_begin = wave_uniform64(r_begin);
+    r_end = wave_uniform64(r_end);
+    int first_doc = 0;
+    unsigned long long first_tile = 0;  // tile position of first_doc's first tile
+    if (r_end > r_begin) {
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < kScoreBlock / kWave; ++j)
+            cnt += __popcll(__ballot(blk_first[j * kWave + lane] <= r_begin));
+        const int k = cnt > 0 ? cnt - 1 : 0;  // (cnt >= 1: blk_first[0] = 0 <= r_begin)
+        const uint32_t nt = tiles_of_len(block_len(k));
+        const unsigned long long first = block_first(k, nt);
+        // Exactly one lane's tiles hold r_begin. The tile walk below stays inside each doc
+        // it takes whatever the scan gave, and with no such lane the wave takes no range.
+        const unsigned long long hit = __ballot(nt > 0u && first <= r_begin && r_begin < first + nt);
+        if (hit) {
+            const int l = __builtin_ctzll(hit);
+            first_doc = k * dpt + l;
+            first_tile = __shfl(first, l);
+        } else {
+            r_end = r_begin;
+        }
+    }
+    first_doc = (int)wave_uniform((uint32_t)first_doc);
+    first_tile = wave_uniform64(first_tile);
+    // The first window of lengths and offsets (doc first_doc + l in lane l).
+    int32_t wlen = 0, woff = 0;
+    {
+        const int i = first_doc + lane;
+        if (i < B) {
+            wlen = lds_len[i];
+            woff = a.off_lds ? lds_off[i] : a.offsets[i];
+        }
+    }
+
     u32x4 qf[NQT][NKS];
 #pragma unroll
     for (int qt = 0; qt < NQT; ++qt)
 #pragma unroll
         for (int s = 0; s < NKS; ++s)
             qf[qt][s] = *reinterpret_cast<const u32x4 *>(qs + (qt * kTileRows + row_in_tile) * LDQ + (s * 4 + kgroup) * 8);
+    // Block wid's lengths, for the scan output written once the first tiles are in flight.
+    const int32_t out_len = (int)wid < kScoreBlock ? block_len((int)wid) : 0;
     __syncthreads();  // the tile slots now reuse the query's LDS (and the prologue's)
 
     // ---- LDS-DMA slots and fragment addresses (the score kernel's layout)
@@ -440,6 +494,24 @@ range_kernel(const RangeArgs a)
     for (int p = 0; p < P; ++p) {
         info[p] = issue((uint32_t)p);
         __builtin_amdgcn_sched_barrier(0);
+    }
+    // For the combine kernel, while the first tiles arrive: S_0 .. S_B (S_B = T), and -inf
+    // for empty docs (no tile, so no piece and no combine); wave w writes block w (and
+    // w + W, ... from global memory when there are fewer than 256 waves).
+    for (int k = (int)wid; k < kScoreBlock; k += (int)W) {
+        int32_t len = out_len;
+        if (k != (int)wid) {
+            const int i = k * dpt + lane;
+            len = lane < dpt && i < B ? a.lengths[i] : 0;
+        }
+        const uint32_t nt = tiles_of_len(len);
+        const unsigned long long first = block_first(k, nt);
+        const int i = k * dpt + lane;
+        if (lane < dpt && i < B) {
+            a.scan[i] = first;
+            if (nt == 0u) a.scores[i] = NEG_INF;
+        }
+        if (k == 0 && lane == 0) a.scan[B] = T;
     }
     uint32_t slot = 0;
     while (info[0] & (1u << 8)) {

@@ -1,9 +1,10 @@
 """The self-scheduling range path that maxsim_rerank takes for a single query of at most
-1024 docs (one register group of query tiles): oracle parity within the tolerance, and
+8192 docs (one register group of query tiles): oracle parity within the tolerance, and
 bit-for-bit equality with the scheduled path (plan, score, combine on a caller
 workspace), which splits docs differently. Batches with empty docs, one-row docs, docs
 far longer than a wave's share, runs of empty docs longer than a 64-doc window, every
-query width up to 128 rows, bf16 and FP8 docs, and the 1024/1025-doc boundary."""
+query width up to 128 rows, bf16 and FP8 docs, prologue blocks of 1 to 32 docs per
+thread, and the 8192/8193-doc boundary."""
 
 from __future__ import annotations
 
@@ -64,8 +65,14 @@ LENGTH_LAWS = {
 }
 
 
-@pytest.mark.parametrize("law", sorted(LENGTH_LAWS))
-@pytest.mark.parametrize("B", [1, 7, 300, 1024])
+# Every law up to 1024 docs (one 4-doc chunk per prologue thread); above that (2 to 8
+# chunks, offsets in LDS or, where they do not fit, from global memory) the laws whose
+# batches stay a few million rows.
+LAW_CASES = [(law, B) for law in sorted(LENGTH_LAWS) for B in (1, 7, 300, 1024)] + [
+    (law, B) for law in ("colbert", "ones", "short", "sparse_long") for B in (1025, 3000, 5000, 8192)]
+
+
+@pytest.mark.parametrize("law,B", LAW_CASES)
 def test_length_laws(law, B):
     _say(f"[range] {law} B={B}")
     r = np.random.default_rng(hash((law, B)) % 2**32)
@@ -101,18 +108,18 @@ def test_runs_of_empty_docs_beyond_a_window():
     check(workloads.custom(32, 128, np.zeros(64, np.int64), seed=11, trailing_gap=5), "all empty")
 
 
-def test_boundary_at_1024_docs():
-    _say("[range] 1024 and 1025 docs")
+def test_boundary_at_8192_docs():
+    _say("[range] 8192 and 8193 docs")
     r = np.random.default_rng(12)
-    lens = r.integers(0, 500, size=1025)
-    w_in = workloads.custom(32, 128, lens[:1024], seed=12, order="shuffled")
+    lens = r.integers(0, 200, size=8193)
+    w_in = workloads.custom(32, 128, lens[:8192], seed=12, order="shuffled")
     w_out = workloads.custom(32, 128, lens, seed=12, order="shuffled")
-    check(w_in, "1024 docs (range path)")
-    check(w_out, "1025 docs (scheduled path)")
+    check(w_in, "8192 docs (range path)")
+    check(w_out, "8193 docs (scheduled path)")
 
 
 def test_named_small_workloads_bitwise_with_the_scheduled_path():
-    for name in ("tiny", "colbert", "long_doc"):
+    for name in ("tiny", "colbert", "long_doc", "scattered"):
         _say(f"[range] {name}")
         check(workloads.make(name), name)
 
