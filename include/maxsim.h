@@ -88,10 +88,11 @@ extern "C" {
  * MaxSim scores, fp16 Q and docs (IEEE binary16).
  * Uses the stream's one-shot workspace (conventions above), so concurrent calls on
  * different streams do not interfere; calls from several host threads are safe.
- * Launches: for 1 <= B <= 8192 with ceil(Lq / 16) <= 8 and ceil(Lq / 16) * ceil(d / 32)
- * <= 32 (the query held in registers at once), a self-scheduling kernel that cuts the docs' 16-row tiles into equal contiguous ranges
- * per wave, then a combine launch for the docs it split; otherwise the staged plan,
- * score and finish below. Both give bitwise the same scores.
+ * Launches: for 1 <= B <= 8192 with ceil(Lq / 16) <= 8 and
+ * ceil(Lq / 16) * ceil(d / 32) <= 32 (the query held in registers at once), a
+ * self-scheduling kernel that cuts the docs' 16-row tiles into equal contiguous
+ * ranges per wave, then a combine launch for the docs it split; otherwise the staged
+ * plan, score and finish below. Both give bitwise the same scores.
  */
 MAXSIM_API int maxsim_rerank(const void *Q, int32_t Lq, int32_t d,
                   const void *docs, int64_t stride,
@@ -128,9 +129,10 @@ MAXSIM_API int maxsim_rerank_short(int dtype, const void *Q, int32_t Lq, int32_t
 
 /*
  * maxsim_rerank for callers that cannot allocate device memory: code under HIP graph
- * capture, tight serving loops, harnesses that forbid hipMalloc. The same plan, score
- * and combine kernels as maxsim_rerank, so the same scores bit for bit, with a fixed
- * scratch array in device memory as their workspace instead of an allocation: 64 MiB
+ * capture, tight serving loops, harnesses that forbid hipMalloc. The same kernels as
+ * maxsim_rerank (the self-scheduling kernel and its combine, or plan, score and
+ * combine, chosen as there), so the same scores bit for bit, with a fixed scratch
+ * array in device memory as their workspace instead of an allocation: 64 MiB
  * per GPU, reserved when the library is first used on that GPU and held until the
  * process ends. The call allocates nothing (no hipMalloc, hipMallocAsync or hipFree).
  * dtype: MAXSIM_F16 or MAXSIM_BF16 (Q and docs); other arguments as maxsim_rerank.
@@ -138,8 +140,9 @@ MAXSIM_API int maxsim_rerank_short(int dtype, const void *Q, int32_t Lq, int32_t
  * that overlap on one GPU (on different streams, or from several host threads before
  * the earlier call's kernels finish) race and give wrong scores; the caller must
  * serialise them, e.g. by issuing them all on one stream.
- * Limit: the schedule must fit in the 64 MiB: 32 bytes per doc, plus the split docs'
- * partial maxima, at most (8 W + min(B, 8 W)) slots of 4 bytes per padded query row (W
+ * Limit: the schedule must fit in the 64 MiB (the self-scheduling kernel's always
+ * does: 8 bytes per doc and two slots per wave). Otherwise 32 bytes per doc, plus the
+ * split docs' partial maxima, at most (8 W + min(B, 8 W)) slots of 4 bytes per padded query row (W
  * the score launch's waves; about 6.3 MB at Lq 32 on MI355X, 8.5 MB for 256 docs at
  * Lq 128), i.e. about 1.8 million docs at Lq <= 32. A larger batch returns
  * MAXSIM_ERR_SCRATCH with nothing enqueued.
