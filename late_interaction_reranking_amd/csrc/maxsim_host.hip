@@ -494,11 +494,19 @@ range_combine_kernel(const RangeCombineArgs a)
 {
     __shared__ f32x4 s_red[kScoreBlock];
     __shared__ f32x4 s_quad[kScoreWaves][kMaxQuads];
-    const unsigned long long T = a.scan[a.B];
-    if (T == 0ull) return;  // every doc empty: no pieces
-    const uint32_t wact = range_active_waves(T, a.waves);
+    typedef __attribute__((address_space(4))) const unsigned long long ConstU64;
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = (int)__builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+    // The tile total and the first doc's scan entries in one round of loads.
+    const int di0 = (int)blockIdx.x * kScoreWaves + wave;
+    const unsigned long long T = ((ConstU64 *)a.scan)[a.B];
+    unsigned long long s0 = 0, e0 = 0;
+    if (di0 < a.B) {
+        s0 = ((ConstU64 *)a.scan)[di0];
+        e0 = ((ConstU64 *)a.scan)[di0 + 1];
+    }
+    if (T == 0ull) return;  // every doc empty: no pieces
+    const uint32_t wact = range_active_waves(T, a.waves);
     const int kgroup = lane >> 4;
     const int lq_pad = a.nqt * kTileRows;
     const int nquads = lq_pad / 4;
@@ -508,10 +516,9 @@ range_combine_kernel(const RangeCombineArgs a)
     f32x4 *red = s_red + wave * kWave;
     f32x4 *rq = s_quad[wave];
     constexpr float NEG_INF = -__builtin_huge_valf();
-    for (int di = (int)blockIdx.x * kScoreWaves + wave; di < a.B; di += (int)gridDim.x * kScoreWaves) {
-        typedef __attribute__((address_space(4))) const unsigned long long ConstU64;
-        const unsigned long long s = ((ConstU64 *)a.scan)[di];
-        const unsigned long long e = ((ConstU64 *)a.scan)[di + 1];
+    for (int di = di0; di < a.B; di += (int)gridDim.x * kScoreWaves) {
+        const unsigned long long s = di == di0 ? s0 : ((ConstU64 *)a.scan)[di];
+        const unsigned long long e = di == di0 ? e0 : ((ConstU64 *)a.scan)[di + 1];
         if (e <= s || e > T) continue;  // no tile (e > T: not a scan the range kernel wrote)
         const uint32_t w_lo = range_wave(s, T, wact);
         const uint32_t w_hi = range_wave(e - 1ull, T, wact);
