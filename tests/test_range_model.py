@@ -7,7 +7,10 @@ finds), and no two pieces share a slot.
 The formulas are the kernel's: W_act = min(W, max(1, T // 2)), wave w's range
 [w T // W_act, (w + 1) T // W_act), the wave of tile t = ceil((t + 1) W_act / T) - 1,
 head slot w for a piece that opens a range, tail slot W_act + w for one that closes it.
-The GPU parity tests exercise the kernels themselves."""
+The prologue's search for each range's first doc (per-thread block sums of up to 32
+docs, a count of block starts, a scan within the block) is checked against a plain
+search over the prefix sums, with its LDS reads inside the region the host sizes. The
+GPU parity tests exercise the kernels themselves."""
 
 import numpy as np
 import pytest
@@ -142,3 +145,79 @@ def test_range_wave_inverts_range_start(T, wact):
         for t in {rb, re - 1, (rb + re) // 2}:
             if rb <= t < re:
                 assert range_wave(t, T, wact) == w
+
+
+# ---- the prologue's search for each wave's first doc, for batches of up to 8192 docs
+
+THREADS = 256
+
+
+def prologue_first_docs(lengths, W):
+    """Each active wave's (first doc, its first tile) as the prologue finds them: thread t
+    sums the tiles of its block of 4 nch docs chunk by chunk from chunk t mod nch on; the
+    blocks' first tiles are their exclusive prefix sums; a wave counts the block starts at
+    or below its first tile, then scans its block's docs. Also returns every LDS index the
+    prologue reads, for the bounds check."""
+    B = len(lengths)
+    nch = -(-B // (4 * THREADS))
+    dpt = 4 * nch
+    nt = np.array([(int(n) + 15) // 16 if n > 0 else 0 for n in lengths] + [0] * (THREADS * dpt - B), np.int64)
+    reads = []
+    mine = np.zeros(THREADS, np.int64)
+    for t in range(THREADS):
+        c = t % nch
+        for j in range(nch):
+            i0 = t * dpt + 4 * c
+            reads.extend(range(i0, i0 + 4))
+            mine[t] += sum(nt[i] for i in range(i0, i0 + 4) if i < B)
+            c = 0 if c + 1 == nch else c + 1
+    blk_first = np.concatenate([[0], np.cumsum(mine)[:-1]])
+    T = int(mine.sum())
+    wact = active(T, W)
+    found = {}
+    for w in range(min(W, wact)):
+        rb = range_start(w, T, wact)
+        re = T if w + 1 == wact else range_start(w + 1, T, wact)
+        if re <= rb:
+            continue
+        k = int(np.sum(blk_first <= rb)) - 1
+        lane_nt = [nt[k * dpt + l] if k * dpt + l < B else 0 for l in range(dpt)]
+        reads.extend(k * dpt + l for l in range(dpt) if k * dpt + l < B)
+        incl = np.cumsum(lane_nt)
+        first = [int(blk_first[k] + incl[l] - lane_nt[l]) for l in range(dpt)]
+        hit = [l for l in range(dpt) if lane_nt[l] > 0 and first[l] <= rb < first[l] + lane_nt[l]]
+        assert len(hit) == 1, (w, rb, hit)
+        found[w] = (k * dpt + hit[0], first[hit[0]])
+    return found, reads, nch
+
+
+def prologue_cases():
+    rng = np.random.default_rng(11)
+    yield np.array([7])
+    yield np.zeros(5, np.int64)
+    yield np.full(8192, 1)
+    yield np.full(8192, 512)
+    for B in (1023, 1024, 1025, 2048, 3000, 5000, 8191, 8192):
+        yield rng.integers(0, 513, size=B)
+    for _ in range(6):
+        B = int(rng.integers(1, 8193))
+        yield np.where(rng.random(B) < 0.7, 0, rng.integers(1, 5000, size=B))
+
+
+@pytest.mark.parametrize("W", [4, 64, 3072])
+def test_prologue_search_finds_each_ranges_first_doc(W):
+    for lengths in prologue_cases():
+        nt = [(int(n) + 15) // 16 if n > 0 else 0 for n in lengths]
+        S = np.concatenate([[0], np.cumsum(nt)]).astype(np.int64)
+        T = int(S[-1])
+        found, reads, nch = prologue_first_docs(lengths, W)
+        if T == 0:
+            assert not found
+            continue
+        wact = active(T, W)
+        for w, (doc, first_tile) in found.items():
+            rb = range_start(w, T, wact)
+            want = int(np.searchsorted(S, rb, side="right") - 1)  # largest i with S_i <= rb
+            assert doc == want and first_tile == int(S[want]) and nt[doc] > 0
+        # every length the prologue reads lies in the LDS region the host sizes for it
+        assert max(reads) < 4 * THREADS * nch
