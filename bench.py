@@ -34,10 +34,12 @@ the score kernel alone.
 --one-shot also times the one-shot entry point (maxsim_rerank, maxsim_rerank_fp8 or
 maxsim_rerank_pairs) with a synchronise after every call, host wall clock per call,
 against the staged path (plan, score, finish on a caller workspace) timed the same way.
+--path one-shot makes the one-shot call itself the timed step (events around the call):
+for one query of at most 8192 docs the self-scheduling range kernel and its combine.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload large]
                     [--no-cpu-baseline] [--no-read-probe] [--copy-probe]
-                    [--flush-reps N] [--one-shot]
+                    [--flush-reps N] [--one-shot] [--path staged|one-shot]
 """
 
 from __future__ import annotations
