@@ -130,7 +130,7 @@ range_kernel(const RangeArgs a)
 
     extern __shared__ __attribute__((aligned(16))) uint16_t qs[];  // Q tile | lengths | offsets; then the tile slots
     __shared__ unsigned long long wave_tiles[kScoreWaves];          // tiles of each wave's docs
-    __shared__ unsigned long long blk_first[kScoreBlock];           // first tile of each thread's block
+    __shared__ unsigned long long blk_excl[kScoreBlock];            // each block's first tile within its wave's
 
     const int lane = threadIdx.x & (kWave - 1);
     const int wave = (int)wave_uniform(threadIdx.x / kWave);
@@ -176,14 +176,7 @@ range_kernel(const RangeArgs a)
         qv[k] = v;
     }
     __builtin_amdgcn_s_waitcnt(kWaitAllVmem);
-#pragma unroll
-    for (int k = 0; k < QL; ++k) {
-        const int e = (int)threadIdx.x + k * kScoreBlock;
-        const int r = e / CPR;
-        const int c = e - r * CPR;
-        if (e < LQP * CPR) *reinterpret_cast<u32x4 *>(qs + r * LDQ + c * 8) = qv[k];
-    }
-    __syncthreads();
+    __syncthreads();  // every wave's lengths are in LDS
 
     // ---- the schedule. Thread t's block of docs is [t dpt, (t + 1) dpt); its tiles are
     // summed chunk by chunk, starting at chunk t mod nch (the threads of a wave then read
@@ -219,17 +212,26 @@ range_kernel(const RangeArgs a)
     const unsigned long long mine = nch <= 2 ? block_tiles(std::integral_constant<int, 2>{})
                                              : block_tiles(std::integral_constant<int, kRangeChunksPerThread>{});
     const unsigned long long incl = wave_scan_incl64(mine);
+    blk_excl[threadIdx.x] = incl - mine;
     if (lane == kWave - 1) wave_tiles[wave] = incl;
-    __syncthreads();
-    unsigned long long before = incl - mine, T = 0;  // first tile of this thread's block; all tiles
+    // The query tile, zero-padded, into LDS (behind the same barrier as the scan).
 #pragma unroll
-    for (int v = 0; v < kScoreWaves; ++v) {
-        const unsigned long long t = wave_tiles[v];
-        if (v < wave) before += t;
-        T += t;
+    for (int k = 0; k < QL; ++k) {
+        const int e = (int)threadIdx.x + k * kScoreBlock;
+        const int r = e / CPR;
+        const int c = e - r * CPR;
+        if (e < LQP * CPR) *reinterpret_cast<u32x4 *>(qs + r * LDQ + c * 8) = qv[k];
     }
-    blk_first[threadIdx.x] = before;
     __syncthreads();
+    // Tiles of each wave's blocks (wave-uniform), all tiles, and the first tile of wave
+    // v's blocks (a sum of selects: an array indexed at run time would go to scratch).
+    static_assert(kScoreWaves == 4, "four waves per workgroup");
+    const unsigned long long wt0 = wave_uniform64(wave_tiles[0]), wt1 = wave_uniform64(wave_tiles[1]),
+                             wt2 = wave_uniform64(wave_tiles[2]), wt3 = wave_uniform64(wave_tiles[3]);
+    const unsigned long long T = wt0 + wt1 + wt2 + wt3;
+    auto wave_first_of = [&](int v) -> unsigned long long {
+        return (v > 0 ? wt0 : 0ull) + (v > 1 ? wt1 : 0ull) + (v > 2 ? wt2 : 0ull);
+    };
 
     // Lane l of block k: doc k dpt + l's length (0 past the block or the batch), tiles and
     // first tile.
@@ -238,7 +240,7 @@ range_kernel(const RangeArgs a)
         return lane < dpt && i < B ? lds_len[i] : 0;
     };
     auto block_first = [&](int k, uint32_t nt) -> unsigned long long {
-        return blk_first[k] + wave_scan_incl64(nt) - nt;
+        return wave_first_of(k / kWave) + blk_excl[k] + wave_scan_incl64(nt) - nt;
     };
 
     // ---- this wave's range and its first doc: the block holding the range's first
@@ -257,8 +259,8 @@ range_kernel(const RangeArgs a)
         int cnt = 0;
 #pragma unroll
         for (int j = 0; j < kScoreBlock / kWave; ++j)
-            cnt += __popcll(__ballot(blk_first[j * kWave + lane] <= r_begin));
-        const int k = cnt > 0 ? cnt - 1 : 0;  // (cnt >= 1: blk_first[0] = 0 <= r_begin)
+            cnt += __popcll(__ballot(wave_first_of(j) + blk_excl[j * kWave + lane] <= r_begin));
+        const int k = cnt > 0 ? cnt - 1 : 0;  // (cnt >= 1: block 0 starts at tile 0 <= r_begin)
         const uint32_t nt = tiles_of_len(block_len(k));
         const unsigned long long first = block_first(k, nt);
         // Exactly one lane's tiles hold r_begin. The tile walk below stays inside each doc
