@@ -166,3 +166,26 @@ def test_repeated_calls_and_streams_are_deterministic():
     torch.cuda.synchronize()
     for o in outs:
         assert torch.equal(o, ref)
+
+
+def test_rows_past_the_32_bit_byte_offsets():
+    """Docs placed from row 2^24 + 5 of a zero-filled 4.3 GB device tensor (row offset
+    times 256 bytes passes 2^32): the range kernel forms its addresses in 64 bits. The
+    oracle scores the same rows at their original offsets (scores do not depend on where
+    the rows sit)."""
+    _say("[range] rows past 2^32 bytes")
+    w = workloads.custom(32, 128, np.random.default_rng(13).integers(0, 300, size=600), seed=13,
+                         order="shuffled", gap=(1, 5))
+    Q, X, offs, lens = upload(w)
+    base = (1 << 24) + 5
+    big = torch.zeros((base + X.shape[0], 128), dtype=X.dtype, device=DEV)
+    big[base:] = X
+    far = offs + base
+    assert int(far.max()) * 128 * 2 > 2 ** 32
+    got = lir.rerank(Q, big, far, lens)
+    ref_staged = staged(Q, big, far, lens)
+    torch.cuda.synchronize()
+    assert_parity(got.cpu().numpy().astype(np.float64), oracle.maxsim_workload(w), "far rows")
+    assert torch.equal(got, ref_staged), "far rows: range path differs from the scheduled path"
+    del big
+    torch.cuda.empty_cache()
