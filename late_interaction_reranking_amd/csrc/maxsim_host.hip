@@ -1090,7 +1090,10 @@ int range_plan(int fmt, int32_t Lq, int32_t d, int32_t B, RangePlan *rp)
     if (score_blocks_per_cu(rp->fn, rp->lds, &per_cu) != MAXSIM_OK) return MAXSIM_ERR_HIP;
     DeviceFacts f;
     if (current_facts(&f) != MAXSIM_OK) return MAXSIM_ERR_HIP;
-    rp->blocks = (uint32_t)(f.cus * per_cu);
+    // (W < 2^16 keeps the cut's 64-bit products in range: the grid is at most 16383
+    // workgroups, more than any device holds at once.)
+    const long long blocks = (long long)f.cus * per_cu;
+    rp->blocks = (uint32_t)(blocks < 16383 ? blocks : 16383);
     const size_t waves = (size_t)rp->blocks * kScoreWaves;
     rp->scan = 0;
     rp->partials = align256((size_t)8 * (B + 1));

@@ -47,7 +47,7 @@ constexpr int kRangeChunksPerThread = 8;                            // most 4-do
 constexpr int kRangeMaxBlockDocs = 4 * kRangeChunksPerThread;       // most docs in a thread's block: 32
 constexpr int kRangeDocsPerChunkRow = 4 * kScoreBlock;              // docs covered per chunk a thread takes
 constexpr int kRangeMaxDocs = kRangeMaxBlockDocs * kScoreBlock;     // docs of a range launch: 8192
-constexpr uint32_t kMinRangeTiles = 2;                           // fewest tiles per active wave
+constexpr uint32_t kMinRangeTiles = 2;                              // fewest tiles per active wave
 
 struct RangeArgs {
     const uint16_t *Q;             // [Lq, d]
@@ -73,8 +73,8 @@ struct RangeCombineArgs {
     float doc_scale;
 };
 
-// Wave w's first tile when T tiles are cut into W_act ranges (T < 2^37, w < 2^16: the
-// products stay below 2^64).
+// Wave w's first tile when T tiles are cut into W_act ranges (T <= B 2^27 <= 2^40 and
+// w, W_act < 2^16: the products stay below 2^56).
 __host__ __device__ inline unsigned long long range_start(uint32_t w, unsigned long long T, uint32_t wact)
 {
     return ((unsigned long long)w * T) / wact;
