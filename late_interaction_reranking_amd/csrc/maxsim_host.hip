@@ -1031,7 +1031,12 @@ int score_launch_waves(int fmt, int32_t Lq, int32_t d, uint32_t *waves)
 bool range_eligible(int32_t Lq, int32_t d, int32_t B)
 {
     if (B < 1 || B > kRangeMaxDocs || Lq < 1) return false;
-    return choose_config(Lq, d).ngroups == 1;
+    if (choose_config(Lq, d).ngroups != 1) return false;
+    // The range kernel's grid has a wave for each of the prologue's 256 doc blocks (at
+    // least one workgroup of 4 waves on each of 64 compute units); a smaller device
+    // takes the scheduled path.
+    DeviceFacts f;
+    return current_facts(&f) == MAXSIM_OK && f.cus * kScoreWaves >= kScoreBlock;
 }
 
 const void *range_fn(int fmt, const Config &c)

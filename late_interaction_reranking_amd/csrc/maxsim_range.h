@@ -498,15 +498,11 @@ range_kernel(const RangeArgs a)
         __builtin_amdgcn_sched_barrier(0);
     }
     // For the combine kernel, while the first tiles arrive: S_0 .. S_B (S_B = T), and -inf
-    // for empty docs (no tile, so no piece and no combine); wave w writes block w (and
-    // w + W, ... from global memory when there are fewer than 256 waves).
-    for (int k = (int)wid; k < kScoreBlock; k += (int)W) {
-        int32_t len = out_len;
-        if (k != (int)wid) {
-            const int i = k * dpt + lane;
-            len = lane < dpt && i < B ? a.lengths[i] : 0;
-        }
-        const uint32_t nt = tiles_of_len(len);
+    // for empty docs (no tile, so no piece and no combine); wave w < 256 writes block w
+    // (the host launches at least 256 waves).
+    if (wid < (uint32_t)kScoreBlock) {
+        const int k = (int)wid;
+        const uint32_t nt = tiles_of_len(out_len);
         const unsigned long long first = block_first(k, nt);
         const int i = k * dpt + lane;
         if (lane < dpt && i < B) {
