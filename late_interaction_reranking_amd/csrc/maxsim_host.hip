@@ -1,8 +1,11 @@
 // C ABI of the MaxSim rerank library (declared in include/maxsim.h): argument checks,
-// the plan (length-binned doc schedule) kernels, the combine kernel (split docs), and
+// the plan (length-binned doc schedule) kernels, the combine kernels (split docs), and
 // the launches of the score kernel for every entry point: one query, a pairs batch
 // (each doc with its own query), several queries over the same docs (passes of query
-// tiles), and FP8 E4M3 docs. The top-k selection lives in maxsim_topk.hip.
+// tiles), and FP8 E4M3 docs. One query against at most 8192 docs takes the
+// self-scheduling range kernel (maxsim_range.h) and its combine instead. The one-shot
+// entry points keep a workspace per (device, stream); maxsim_rerank_noalloc uses a
+// static per-device scratch. The top-k selection lives in maxsim_topk.hip.
 #include "maxsim.h"
 
 #include <string.h>
